@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for the selective-SSM scan (shared by the GPU path's
+tests/bench and the oracle; holds none of the scan's arithmetic).
+
+Recipe (the pages measure on trained Mamba / Falcon-Mamba / Zamba layers over
+2K-64K contexts -- "Scaling State-Space Models on Multiple GPUs with Tensor
+Parallelism", Methodology item 5 -- these synthetic layers stand in for them):
+  x, z, B, C ~ N(0, 1)                 dt (raw step) ~ N(0, 0.5^2)
+  per channel: dt0 log-uniform in [lo, hi], dt_bias = log(expm1(dt0))
+  A[c, n] = -exp(A_log[n]), A_log[n] = log(n + 1)
+  Dskip = 1, conv_w ~ U(-0.5, 0.5), conv_b = 0
+  B and C are shared by all channels of a batch row (per token, per state).
+io tensors are drawn in fp32 and rounded to bf16 (round-to-nearest-even) when
+io is bf16; parameters are fp32.  Every tensor has its own stream, keyed by
+(seed, tensor name, step), so a decode token's inputs do not depend on L.
+"""
+from __future__ import annotations
+
+import zlib
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+CONV_W = 4
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    seqlen: int
+    d_inner: int
+    d_state: int
+    io: str                      # "f32" or "bf16"
+    dt_range: Tuple[float, float] = (1e-3, 1e-1)
+    decode_steps: int = 0
+    note: str = ""
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 64, 16, 4, "f32", note="tiny fp32 case the oracle runs in milliseconds"),
+    "mamba130m": Workload("mamba130m", 4, 2048, 1536, 16, "bf16", note="Mamba-130M-shaped layer, prefill"),
+    "mamba2.8b": Workload("mamba2.8b", 64, 8192, 5120, 16, "bf16", decode_steps=256,
+                          note="Mamba-2.8B-shaped layer, prefill then 256 decode steps"),
+    "slice7b": Workload("slice7b", 1, 32768, 2048, 16, "bf16", decode_steps=128,
+                        note="7B-class channel slice (2048 of 8192 channels), prefill then 128 decode steps"),
+    "long64k": Workload("long64k", 2, 65536, 7424, 16, "bf16", dt_range=(1e-4, 1e-1),
+                        note="long context, prefill only"),
+}
+
+
+def io_dtype(io: str) -> torch.dtype:
+    if io == "f32":
+        return torch.float32
+    if io == "bf16":
+        return torch.bfloat16
+    raise ValueError(f"unknown io dtype {io!r}")
+
+
+def _key(k) -> int:
+    return zlib.crc32(k.encode()) if isinstance(k, str) else int(k)
+
+
+def rng(seed: int, *keys) -> np.random.Generator:
+    """Independent PCG64 stream for (seed, *keys)."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed)] + [_key(k) for k in keys])))
+
+
+def torch_seed(seed: int, *keys) -> int:
+    ss = np.random.SeedSequence([int(seed)] + [_key(k) for k in keys])
+    return int(ss.generate_state(1, np.uint64)[0] & np.uint64(2**63 - 1))
+
+
+def make_params(d_inner: int, d_state: int, seed: int = 0,
+                dt_range: Tuple[float, float] = (1e-3, 1e-1)) -> dict:
+    """Per-channel parameters, fp32 torch tensors on the host."""
+    D, N = d_inner, d_state
+    lo, hi = dt_range
+    g = rng(seed, "dt0")
+    dt0 = np.exp(g.uniform(np.log(lo), np.log(hi), size=D))
+    dt_bias = np.log(np.expm1(dt0))
+    A_log = np.log(np.arange(1, N + 1, dtype=np.float64))
+    A = np.broadcast_to(-np.exp(A_log), (D, N))
+    conv_w = rng(seed, "conv_w").uniform(-0.5, 0.5, size=(D, CONV_W))
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return {"A": f(A), "Dskip": f(np.ones(D)), "dt_bias": f(dt_bias),
+            "conv_w": f(conv_w), "conv_b": f(np.zeros(D))}
+
+
+def make_sequence(batch: int, seqlen: int, d_inner: int, d_state: int, io: str = "bf16",
+                  seed: int = 0, stream="prefill", dt_std: float = 0.5) -> dict:
+    """x, dt, z [B, D, L] and Bm, Cm [B, L, N] as host torch tensors of the io dtype."""
+    Bsz, L, D, N = batch, seqlen, d_inner, d_state
+    dtype = io_dtype(io)
+
+    def normal(name, shape, scale=1.0):
+        a = rng(seed, stream, name).standard_normal(size=shape, dtype=np.float32)
+        if scale != 1.0:
+            a *= np.float32(scale)
+        return torch.from_numpy(a).to(dtype)
+
+    return {"x": normal("x", (Bsz, D, L)), "dt": normal("dt", (Bsz, D, L), dt_std),
+            "z": normal("z", (Bsz, D, L)), "Bm": normal("B", (Bsz, L, N)),
+            "Cm": normal("C", (Bsz, L, N))}
+
+
+def make_sequence_device(batch: int, seqlen: int, d_inner: int, d_state: int, io: str = "bf16",
+                         seed: int = 0, stream="prefill", device="cuda", dt_std: float = 0.5) -> dict:
+    """Same recipe generated with torch's device RNG, for sizes too large to draw on the host.
+
+    The values differ from ``make_sequence`` (another generator) but have the
+    same distributions; they are seeded and reproducible on one torch build.
+    """
+    Bsz, L, D, N = batch, seqlen, d_inner, d_state
+    dtype = io_dtype(io)
+
+    def normal(name, shape, scale=1.0):
+        g = torch.Generator(device=device)
+        g.manual_seed(torch_seed(seed, stream, name))
+        out = torch.empty(shape, dtype=dtype, device=device)
+        # draw in row chunks to bound the fp32 temporary
+        flat = out.view(shape[0], -1)
+        for i in range(shape[0]):
+            t = torch.randn(flat.shape[1], generator=g, device=device, dtype=torch.float32)
+            if scale != 1.0:
+                t.mul_(scale)
+            flat[i].copy_(t)
+            del t
+        return out
+
+    return {"x": normal("x", (Bsz, D, L)), "dt": normal("dt", (Bsz, D, L), dt_std),
+            "z": normal("z", (Bsz, D, L)), "Bm": normal("B", (Bsz, L, N)),
+            "Cm": normal("C", (Bsz, L, N))}
+
+
+def make_decode_token(batch: int, d_inner: int, d_state: int, step: int, io: str = "bf16",
+                      seed: int = 0) -> dict:
+    """Inputs of decode step ``step``: x, dt, z [B, D]; Bm, Cm [B, N]."""
+    s = make_sequence(batch, 1, d_inner, d_state, io, seed, stream=f"decode{step}")
+    return {"x": s["x"][..., 0].contiguous(), "dt": s["dt"][..., 0].contiguous(),
+            "z": s["z"][..., 0].contiguous(), "Bm": s["Bm"][:, 0].contiguous(),
+            "Cm": s["Cm"][:, 0].contiguous()}
