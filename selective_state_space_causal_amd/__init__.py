@@ -1,1 +1,8 @@
-"""MI355X-native selective state-space causal scan (prefill + decode) for one GPU channel slice."""
+"""MI355X-native selective state-space causal scan (prefill + decode) for one GPU's channel slice.
+
+``prefill`` and ``decode_step`` call the C ABI of include/ssm.h (libssm.so, hand-written
+HIP kernels for gfx950) through a thin ctypes binding; ``inputs`` makes seeded synthetic
+workloads.  Importing the package does not load the library; the first call does, and
+raises if it is not built.
+"""
+from ._lib import SsmError, decode_step, load, prefill, workspace_bytes  # noqa: F401

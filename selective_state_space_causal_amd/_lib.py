@@ -1,0 +1,173 @@
+"""ctypes binding of libssm.so (include/ssm.h).  Argument marshalling only: every step of
+the scan runs in the library's HIP kernels.  PyTorch supplies device memory and the
+current HIP stream.  There is no fallback: a missing library raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+ABI_VERSION = 1
+MAX_STATE = 16
+CONV_W = 4
+
+STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE", 4: "SSM_ERR_ALIGN",
+          5: "SSM_ERR_ALIAS", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_LAUNCH"}
+
+
+class SsmError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_inner", ctypes.c_int64),
+                ("d_state", ctypes.c_int64), ("d_conv", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+                ("chunk_hint", ctypes.c_int32)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("Dskip", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libssm.so and declare its entry points (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
+                          "(or python selective_state_space_causal_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.ssm_abi_version.restype = ctypes.c_int
+    lib.ssm_abi_version.argtypes = []
+    lib.ssm_status_str.restype = ctypes.c_char_p
+    lib.ssm_status_str.argtypes = [ctypes.c_int]
+    lib.ssm_prefill_workspace_bytes.restype = sz
+    lib.ssm_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+    lib.ssm_prefill.restype = ctypes.c_int
+    lib.ssm_prefill.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params)] + [vp] * 11 + [sz, vp]
+    lib.ssm_decode_step.restype = ctypes.c_int
+    lib.ssm_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params)] + [vp] * 9
+    if lib.ssm_abi_version() != ABI_VERSION:
+        raise ImportError(f"libssm ABI {lib.ssm_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return SSM_F32
+    if dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"io tensors must be float32 or bfloat16, got {dtype}")
+
+
+def _check(t: Optional[torch.Tensor], name: str, shape, dtype, device, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+
+
+def make_params(params: dict) -> Params:
+    return Params(params["A"].data_ptr(), params["Dskip"].data_ptr(), params["dt_bias"].data_ptr(),
+                  params["conv_w"].data_ptr(),
+                  None if params.get("conv_b") is None else params["conv_b"].data_ptr())
+
+
+def _check_params(params: dict, D: int, N: int, device):
+    f32 = torch.float32
+    _check(params["A"], "A", (D, N), f32, device)
+    _check(params["Dskip"], "Dskip", (D,), f32, device)
+    _check(params["dt_bias"], "dt_bias", (D,), f32, device)
+    _check(params["conv_w"], "conv_w", (D, CONV_W), f32, device)
+    _check(params.get("conv_b"), "conv_b", (D,), f32, device, optional=True)
+
+
+def stream_handle(stream=None) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype=torch.bfloat16, chunk_hint=0) -> int:
+    d = Dims(batch, seqlen, d_inner, d_state, CONV_W, _io_code(io_dtype), chunk_hint)
+    return int(load().ssm_prefill_workspace_bytes(ctypes.byref(d)))
+
+
+def prefill(x, dt, z, Bm, Cm, params: dict, h0=None, conv0=None, *, chunk_hint: int = 0,
+            y=None, h_out=None, conv_out=None, workspace=None, stream=None):
+    """ssm_prefill.  x, dt, z [B, D, L] and Bm, Cm [B, L, N] (io dtype, on the GPU); z may be
+    None.  Returns (y, h_out, conv_out); outputs are allocated when not given."""
+    lib = load()
+    Bsz, D, L = x.shape
+    N = params["A"].shape[1]
+    dev, io = x.device, x.dtype
+    for t, n in ((x, "x"), (dt, "dt"), (z, "z")):
+        _check(t, n, (Bsz, D, L), io, dev, optional=(n == "z"))
+    _check(Bm, "Bm", (Bsz, L, N), io, dev)
+    _check(Cm, "Cm", (Bsz, L, N), io, dev)
+    _check(h0, "h0", (Bsz, D, N), torch.float32, dev, optional=True)
+    _check(conv0, "conv0", (Bsz, D, CONV_W - 1), torch.float32, dev, optional=True)
+    _check_params(params, D, N, dev)
+    y = torch.empty_like(x) if y is None else y
+    h_out = torch.empty(Bsz, D, N, dtype=torch.float32, device=dev) if h_out is None else h_out
+    conv_out = torch.empty(Bsz, D, CONV_W - 1, dtype=torch.float32, device=dev) if conv_out is None else conv_out
+    d = Dims(Bsz, L, D, N, CONV_W, _io_code(io), chunk_hint)
+    need = int(lib.ssm_prefill_workspace_bytes(ctypes.byref(d)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p = make_params(params)
+    st = lib.ssm_prefill(ctypes.byref(d), ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(z), _ptr(Bm), _ptr(Cm),
+                         _ptr(h0), _ptr(conv0), _ptr(y), _ptr(h_out), _ptr(conv_out), _ptr(workspace),
+                         ws_bytes, stream_handle(stream))
+    if st != 0:
+        raise SsmError("ssm_prefill", st, lib.ssm_status_str(st).decode())
+    return y, h_out, conv_out
+
+
+def decode_step(x_t, dt_t, z_t, B_t, C_t, params: dict, h, conv, *, y_t=None, stream=None):
+    """ssm_decode_step: x_t, dt_t, z_t [B, D]; B_t, C_t [B, N]; h [B, D, N] and conv [B, D, 3]
+    are updated in place.  Returns y_t [B, D]."""
+    lib = load()
+    Bsz, D = x_t.shape
+    N = params["A"].shape[1]
+    dev, io = x_t.device, x_t.dtype
+    for t, n in ((x_t, "x_t"), (dt_t, "dt_t"), (z_t, "z_t")):
+        _check(t, n, (Bsz, D), io, dev, optional=(n == "z_t"))
+    _check(B_t, "B_t", (Bsz, N), io, dev)
+    _check(C_t, "C_t", (Bsz, N), io, dev)
+    _check(h, "h", (Bsz, D, N), torch.float32, dev)
+    _check(conv, "conv", (Bsz, D, CONV_W - 1), torch.float32, dev)
+    _check_params(params, D, N, dev)
+    y_t = torch.empty_like(x_t) if y_t is None else y_t
+    d = Dims(Bsz, 1, D, N, CONV_W, _io_code(io), 0)
+    p = make_params(params)
+    st = lib.ssm_decode_step(ctypes.byref(d), ctypes.byref(p), _ptr(x_t), _ptr(dt_t), _ptr(z_t), _ptr(B_t),
+                             _ptr(C_t), _ptr(y_t), _ptr(h), _ptr(conv), stream_handle(stream))
+    if st != 0:
+        raise SsmError("ssm_decode_step", st, lib.ssm_status_str(st).decode())
+    return y_t

@@ -1,0 +1,199 @@
+// ssm_api.hip -- the C ABI declared in include/ssm.h: argument validation on the host
+// (before any HIP call), choice of decomposition, and launches on the caller's stream.
+#include <string.h>
+
+#include "../../include/ssm.h"
+#include "ssm_internal.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi), empty when lo == hi
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+// bytes = n0 * n1 * n2 * esize, false on overflow
+bool tensor_bytes(int64_t n0, int64_t n1, int64_t n2, int64_t esize, int64_t* bytes) {
+  int64_t t;
+  return mul_ok(n0, n1, &t) && mul_ok(t, n2, &t) && mul_ok(t, esize, bytes);
+}
+
+Range span(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, p ? lo + (uintptr_t)bytes : lo};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape / dtype checks shared by both entry points.  L is validated only when use_L.
+int check_dims(const ssm_dims* d, bool use_L) {
+  if (!d) return SSM_ERR_NULL;
+  if (d->batch < 1 || d->d_inner < 1 || d->d_state < 1 || d->d_state > SSM_MAX_STATE ||
+      d->d_conv != SSM_CONV_WIDTH || (use_L && d->seqlen < 1) || d->chunk_hint < 0)
+    return SSM_ERR_SHAPE;
+  if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  // Every byte count the kernels index must fit comfortably in int64.
+  const int64_t L = use_L ? d->seqlen : 1, es = d->io_dtype == SSM_BF16 ? 2 : 4;
+  int64_t bytes;
+  if (!tensor_bytes(d->batch, d->d_inner, L, es, &bytes) || !tensor_bytes(d->batch, L, d->d_state, es, &bytes) ||
+      !tensor_bytes(d->batch, d->d_inner, d->d_state, 4, &bytes) || (d->batch * d->d_inner) > (int64_t)INT32_MAX * 256)
+    return SSM_ERR_SHAPE;
+  return SSM_OK;
+}
+
+int check_params(const ssm_params* p, const void* const* outs, const int64_t* out_bytes, int nouts, int64_t D,
+                 int64_t N) {
+  if (!p || !p->A || !p->Dskip || !p->dt_bias || !p->conv_w) return SSM_ERR_NULL;
+  const void* ptrs[5] = {p->A, p->Dskip, p->dt_bias, p->conv_w, p->conv_b};
+  const int64_t bytes[5] = {D * N * 4, D * 4, D * 4, D * 4 * 4, D * 4};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) continue;
+    if (!aligned16(ptrs[i])) return SSM_ERR_ALIGN;
+    for (int o = 0; o < nouts; ++o)
+      if (overlaps(span(ptrs[i], bytes[i]), span(outs[o], out_bytes[o]))) return SSM_ERR_ALIAS;
+  }
+  return SSM_OK;
+}
+
+ssm::ScanArgs make_args(const ssm_dims* d, const ssm_params* p) {
+  ssm::ScanArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = p->A;
+  a.Dskip = p->Dskip;
+  a.dt_bias = p->dt_bias;
+  a.conv_w = p->conv_w;
+  a.conv_b = p->conv_b;
+  a.B = d->batch;
+  a.L = d->seqlen;
+  a.D = d->d_inner;
+  a.N = (int)d->d_state;
+  a.bf16 = d->io_dtype == SSM_BF16;
+  a.chunk_hint = d->chunk_hint;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_str(int s) {
+  switch (s) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "invalid sizes (batch/seqlen/d_inner >= 1, 1 <= d_state <= 16, d_conv == 4)";
+    case SSM_ERR_DTYPE: return "io_dtype must be SSM_F32 or SSM_BF16";
+    case SSM_ERR_ALIGN: return "tensor base pointers must be 16-byte aligned";
+    case SSM_ERR_ALIAS: return "an output overlaps an input or another output";
+    case SSM_ERR_WORKSPACE: return "workspace missing or smaller than ssm_prefill_workspace_bytes()";
+    case SSM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t ssm_prefill_workspace_bytes(const ssm_dims* d) {
+  if (check_dims(d, true) != SSM_OK) return 0;
+  ssm_params none;
+  memset(&none, 0, sizeof none);
+  return ssm::prefill_workspace_bytes(make_args(d, &none));
+}
+
+int ssm_prefill(const ssm_dims* d, const ssm_params* p, const void* x, const void* dt, const void* z,
+                const void* Bm, const void* Cm, const float* h0, const float* conv0, void* y, float* h_out,
+                float* conv_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(d, true);
+  if (st != SSM_OK) return st;
+  if (!x || !dt || !Bm || !Cm || !y || !h_out || !conv_out) return SSM_ERR_NULL;
+  const int64_t B = d->batch, L = d->seqlen, D = d->d_inner, N = d->d_state;
+  const int64_t es = d->io_dtype == SSM_BF16 ? 2 : 4;
+  const int64_t seq = B * D * L * es, bc = B * L * N * es, hb = B * D * N * 4, cvb = B * D * 3 * 4;
+
+  const void* ins[7] = {x, dt, z, Bm, Cm, h0, conv0};
+  const int64_t in_bytes[7] = {seq, seq, seq, bc, bc, hb, cvb};
+  const void* outs[3] = {y, h_out, conv_out};
+  const int64_t out_bytes[3] = {seq, hb, cvb};
+  for (int i = 0; i < 7; ++i)
+    if (ins[i] && !aligned16(ins[i])) return SSM_ERR_ALIGN;
+  for (int o = 0; o < 3; ++o)
+    if (!aligned16(outs[o])) return SSM_ERR_ALIGN;
+  st = check_params(p, outs, out_bytes, 3, D, N);
+  if (st != SSM_OK) return st;
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(span(outs[o], out_bytes[o]), span(ins[i], in_bytes[i]))) return SSM_ERR_ALIAS;
+    for (int q = o + 1; q < 3; ++q)
+      if (overlaps(span(outs[o], out_bytes[o]), span(outs[q], out_bytes[q]))) return SSM_ERR_ALIAS;
+  }
+
+  ssm::ScanArgs a = make_args(d, p);
+  a.x = x;
+  a.dt = dt;
+  a.z = z;
+  a.Bm = Bm;
+  a.Cm = Cm;
+  a.h0 = h0;
+  a.conv0 = conv0;
+  a.y = y;
+  a.h_out = h_out;
+  a.conv_out = conv_out;
+  const size_t need = ssm::prefill_workspace_bytes(a);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SSM_ERR_ALIGN;
+    const Range ws = span(workspace, (int64_t)need);
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(ws, span(ins[i], in_bytes[i]))) return SSM_ERR_ALIAS;
+    for (int o = 0; o < 3; ++o)
+      if (overlaps(ws, span(outs[o], out_bytes[o]))) return SSM_ERR_ALIAS;
+  }
+  (void)hipGetLastError();  // drop a stale error so a launch failure is reported as ours
+  if (ssm::launch_prefill(a, workspace, static_cast<hipStream_t>(stream)) != hipSuccess) return SSM_ERR_LAUNCH;
+  return SSM_OK;
+}
+
+int ssm_decode_step(const ssm_dims* d, const ssm_params* p, const void* x_t, const void* dt_t, const void* z_t,
+                    const void* B_t, const void* C_t, void* y_t, float* h, float* conv_state, void* stream) {
+  int st = check_dims(d, false);
+  if (st != SSM_OK) return st;
+  if (!x_t || !dt_t || !B_t || !C_t || !y_t || !h || !conv_state) return SSM_ERR_NULL;
+  const int64_t B = d->batch, D = d->d_inner, N = d->d_state;
+  const int64_t es = d->io_dtype == SSM_BF16 ? 2 : 4;
+  const int64_t tok = B * D * es, bc = B * N * es, hb = B * D * N * 4, cvb = B * D * 3 * 4;
+  const void* ins[5] = {x_t, dt_t, z_t, B_t, C_t};
+  const int64_t in_bytes[5] = {tok, tok, tok, bc, bc};
+  const void* outs[3] = {y_t, h, conv_state};
+  const int64_t out_bytes[3] = {tok, hb, cvb};
+  for (int i = 0; i < 5; ++i)
+    if (ins[i] && !aligned16(ins[i])) return SSM_ERR_ALIGN;
+  for (int o = 0; o < 3; ++o)
+    if (!aligned16(outs[o])) return SSM_ERR_ALIGN;
+  st = check_params(p, outs, out_bytes, 3, D, N);
+  if (st != SSM_OK) return st;
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(span(outs[o], out_bytes[o]), span(ins[i], in_bytes[i]))) return SSM_ERR_ALIAS;
+    for (int q = o + 1; q < 3; ++q)
+      if (overlaps(span(outs[o], out_bytes[o]), span(outs[q], out_bytes[q]))) return SSM_ERR_ALIAS;
+  }
+  ssm::ScanArgs a = make_args(d, p);
+  a.L = 1;
+  a.x = x_t;
+  a.dt = dt_t;
+  a.z = z_t;
+  a.Bm = B_t;
+  a.Cm = C_t;
+  a.h0 = h;
+  a.conv0 = conv_state;
+  a.y = y_t;
+  a.h_out = h;
+  a.conv_out = conv_state;
+  (void)hipGetLastError();
+  if (ssm::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return SSM_ERR_LAUNCH;
+  return SSM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,204 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_causal_amd as ssm
+from selective_state_space_causal_amd import inputs as I
+from tests.gpu_common import DEV, TAU, assert_bitwise, assert_close, dev, f64, note, sample_pairs, threads
+
+pytestmark = pytest.mark.gpu
+
+
+def run(seq, prm, gate=True, **kw):
+    s = dev(seq)
+    return ssm.prefill(s["x"], s["dt"], s["z"] if gate else None, s["Bm"], s["Cm"], dev(prm), **kw)
+
+
+def check_full(seq, prm, io, gate=True, what="", **kw):
+    y, h, c = run(seq, prm, gate, **kw)
+    torch.cuda.synchronize()
+    yr, hr, cr = oracle.prefill(seq, prm, nthreads=threads(), gate=gate)
+    ey = assert_close(y, yr, TAU[io], f"{what} y")
+    eh = assert_close(h, hr, TAU[io], f"{what} h")
+    assert_bitwise(c, cr, f"{what} conv")
+    return ey, eh
+
+
+def test_tiny_fp32_workload():
+    w = I.WORKLOADS["tiny"]
+    note(f"tiny: B={w.batch} L={w.seqlen} D={w.d_inner} N={w.d_state} {w.io}")
+    prm = I.make_params(w.d_inner, w.d_state)
+    seq = I.make_sequence(w.batch, w.seqlen, w.d_inner, w.d_state, w.io)
+    ey, eh = check_full(seq, prm, w.io, what="tiny")
+    note(f"tiny max err y {ey:.2e} h {eh:.2e}")
+
+
+def test_mamba130m_workload_full_tensors():
+    w = I.WORKLOADS["mamba130m"]
+    note(f"mamba130m: B={w.batch} L={w.seqlen} D={w.d_inner} N={w.d_state} {w.io}")
+    prm = I.make_params(w.d_inner, w.d_state)
+    seq = I.make_sequence(w.batch, w.seqlen, w.d_inner, w.d_state, w.io)
+    ey, eh = check_full(seq, prm, w.io, what="mamba130m")
+    note(f"mamba130m max err y {ey:.2e} h {eh:.2e}")
+
+
+EDGE = [
+    # B, L, D, N, io, gate, conv_b
+    (1, 1, 1, 1, "f32", True, True), (1, 2, 3, 4, "f32", False, True), (2, 3, 5, 16, "bf16", True, False),
+    (3, 4, 65, 16, "bf16", True, True), (1, 5, 64, 15, "f32", True, True), (2, 63, 130, 16, "bf16", False, True),
+    (1, 64, 7, 8, "f32", True, False), (2, 65, 64, 16, "bf16", True, True), (1, 127, 33, 16, "f32", True, True),
+    (1, 513, 3, 16, "bf16", True, True), (1, 1000, 66, 3, "f32", True, True), (3, 777, 129, 16, "bf16", True, True),
+]
+
+
+@pytest.mark.parametrize("B,L,D,N,io,gate,cb", EDGE)
+def test_edge_shapes(B, L, D, N, io, gate, cb):
+    note(f"edge B={B} L={L} D={D} N={N} {io} gate={gate} conv_b={cb}")
+    prm = I.make_params(D, N, seed=L + D)
+    prm["conv_b"] = prm["conv_b"] + 0.1 if cb else None
+    seq = I.make_sequence(B, L, D, N, io, seed=B + 7 * L)
+    check_full(seq, prm, io, gate, what=f"edge{B},{L},{D},{N}")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_chunked_prefill_from_cache(io):
+    """prefill(L1) then prefill(L2) resumed from its cache == prefill(L1 + L2)."""
+    B, D, N, L1, L2 = 2, 70, 16, 300, 211
+    note(f"chunked prefill {io}")
+    prm = I.make_params(D, N, seed=3)
+    seq = I.make_sequence(B, L1 + L2, D, N, io, seed=3)
+    part = lambda s, a, b: {k: (v[:, :, a:b] if k in ("x", "dt", "z") else v[:, a:b]).contiguous()
+                            for k, v in s.items()}
+    y1, h1, c1 = run(part(seq, 0, L1), prm)
+    s2 = dev(part(seq, L1, L1 + L2))
+    y2, h2, c2 = ssm.prefill(s2["x"], s2["dt"], s2["z"], s2["Bm"], s2["Cm"], dev(prm), h0=h1, conv0=c1)
+    torch.cuda.synchronize()
+    yr, hr, cr = oracle.prefill(seq, prm, nthreads=threads())
+    assert_close(torch.cat([y1, y2], 2), yr, TAU[io], "chunked y")
+    assert_close(h2, hr, TAU[io], "chunked h")
+    assert_bitwise(c2, cr, "chunked conv")
+
+
+@pytest.mark.parametrize("io,B,D,N", [("f32", 2, 40, 16), ("bf16", 3, 130, 16), ("bf16", 1, 5, 3)])
+def test_decode_steps_match_oracle(io, B, D, N):
+    """Prefill, then T single-token steps from the cache; y, h each step, conv bitwise each step."""
+    L, T = 97, 24
+    note(f"decode {io} B={B} D={D} N={N}")
+    prm = I.make_params(D, N, seed=5)
+    seq = I.make_sequence(B, L, D, N, io, seed=5)
+    _, h, c = run(seq, prm)
+    _, hr, cr = oracle.prefill(seq, prm)
+    pd = dev(prm)
+    for t in range(T):
+        tok = I.make_decode_token(B, D, N, t, io, seed=5)
+        td = dev(tok)
+        y = ssm.decode_step(td["x"], td["dt"], td["z"], td["Bm"], td["Cm"], pd, h, c)
+        yr, hr, cr = oracle.decode_step(tok, prm, hr, cr)
+        assert_close(y, yr, TAU[io], f"decode y step {t}")
+        assert_close(h, hr, TAU[io], f"decode h step {t}")
+        assert_bitwise(c, cr, f"decode conv step {t}")
+
+
+def test_decode_equals_longer_prefill():
+    """State caching invariant on the GPU: prefill(L1) + L2 decode steps == prefill(L1 + L2)."""
+    B, D, N, L1, L2 = 2, 96, 16, 200, 40
+    prm = I.make_params(D, N, seed=9)
+    seq = I.make_sequence(B, L1 + L2, D, N, "bf16", seed=9)
+    yf, hf, cf = run(seq, prm)
+    s = dev(seq)
+    _, h, c = ssm.prefill(s["x"][:, :, :L1].contiguous(), s["dt"][:, :, :L1].contiguous(),
+                          s["z"][:, :, :L1].contiguous(), s["Bm"][:, :L1].contiguous(),
+                          s["Cm"][:, :L1].contiguous(), dev(prm))
+    pd = dev(prm)
+    for t in range(L1, L1 + L2):
+        y = ssm.decode_step(s["x"][:, :, t].contiguous(), s["dt"][:, :, t].contiguous(), s["z"][:, :, t].contiguous(),
+                            s["Bm"][:, t].contiguous(), s["Cm"][:, t].contiguous(), pd, h, c)
+        assert_close(y, f64(yf[:, :, t]), TAU["bf16"], f"step {t} vs prefill")
+    assert_close(h, f64(hf), 1e-4, "h after decode vs prefill")
+    assert_bitwise(c, f64(cf), "conv after decode vs prefill")
+
+
+def test_channel_and_batch_slices_are_bitwise():
+    """Channel locality on the GPU: a channel slice (or batch row) run alone reproduces the
+    full run bit for bit when the decomposition is pinned with chunk_hint."""
+    B, L, D, N = 3, 300, 200, 16
+    prm = I.make_params(D, N, seed=11)
+    seq = I.make_sequence(B, L, D, N, "bf16", seed=11)
+    y, h, c = run(seq, prm, chunk_hint=1)
+    for lo, hi in ((0, 64), (64, 65), (65, 200)):
+        ps = {k: v[lo:hi].contiguous() for k, v in prm.items()}
+        ss = {k: (v[:, lo:hi].contiguous() if k in ("x", "dt", "z") else v) for k, v in seq.items()}
+        ys, hs, cs = run(ss, ps, chunk_hint=1)
+        assert torch.equal(ys.view(torch.int16), y[:, lo:hi].view(torch.int16))
+        assert torch.equal(hs, h[:, lo:hi]) and torch.equal(cs, c[:, lo:hi])
+    for b in range(B):
+        sb = {k: v[b:b + 1].contiguous() for k, v in seq.items()}
+        yb, hb, _ = run(sb, prm, chunk_hint=1)
+        assert torch.equal(yb.view(torch.int16), y[b:b + 1].view(torch.int16)) and torch.equal(hb, h[b:b + 1])
+
+
+def test_pow2_scaling_bitwise():
+    """Dskip = 0: doubling C doubles y; doubling B doubles h and y (exact in binary fp)."""
+    B, L, D, N = 2, 150, 70, 16
+    prm = I.make_params(D, N, seed=13)
+    prm["Dskip"] = torch.zeros_like(prm["Dskip"])
+    seq = I.make_sequence(B, L, D, N, "f32", seed=13)
+    y, h, _ = run(seq, prm)
+    y2, h2, _ = run(dict(seq, Cm=seq["Cm"] * 2), prm)
+    assert torch.equal(y2, 2 * y) and torch.equal(h2, h)
+    y3, h3, _ = run(dict(seq, Bm=seq["Bm"] * 2), prm)
+    assert torch.equal(h3, 2 * h) and torch.equal(y3, 2 * y)
+
+
+def test_deterministic_and_in_bounds():
+    """Two runs are bitwise equal, and nothing is written outside the outputs (canaries)."""
+    B, L, D, N = 2, 333, 97, 16
+    prm = dev(I.make_params(D, N, seed=17))
+    s = dev(I.make_sequence(B, L, D, N, "bf16", seed=17))
+    pad = 4096
+    outs = []
+    for _ in range(2):
+        ybuf = torch.full((B * D * L + 2 * pad,), 12345.0, dtype=torch.bfloat16, device=DEV)
+        hbuf = torch.full((B * D * N + 2 * pad,), -7.0, device=DEV)
+        cbuf = torch.full((B * D * 3 + 2 * pad,), -9.0, device=DEV)
+        y = ybuf[pad:pad + B * D * L].view(B, D, L)
+        h = hbuf[pad:pad + B * D * N].view(B, D, N)
+        c = cbuf[pad:pad + B * D * 3].view(B, D, 3)
+        ssm.prefill(s["x"], s["dt"], s["z"], s["Bm"], s["Cm"], prm, y=y, h_out=h, conv_out=c)
+        torch.cuda.synchronize()
+        for buf, val in ((ybuf, 12345.0), (hbuf, -7.0), (cbuf, -9.0)):
+            assert torch.all(buf[:pad] == val) and torch.all(buf[-pad:] == val), "write outside an output"
+        outs.append((y.clone(), h.clone(), c.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_cache_roundtrip_through_host():
+    """Copying the cache to the host and back, then resuming, equals resuming directly."""
+    B, L, D, N = 1, 100, 64, 16
+    prm = dev(I.make_params(D, N, seed=19))
+    s = dev(I.make_sequence(B, L, D, N, "bf16", seed=19))
+    _, h, c = ssm.prefill(s["x"], s["dt"], s["z"], s["Bm"], s["Cm"], prm)
+    h2, c2 = h.cpu().to(DEV), c.cpu().to(DEV)
+    tok = dev(I.make_decode_token(B, D, N, 0, "bf16", seed=19))
+    ya = ssm.decode_step(tok["x"], tok["dt"], tok["z"], tok["Bm"], tok["Cm"], prm, h, c)
+    yb = ssm.decode_step(tok["x"], tok["dt"], tok["z"], tok["Bm"], tok["Cm"], prm, h2, c2)
+    assert torch.equal(ya.view(torch.int16), yb.view(torch.int16)) and torch.equal(h, h2) and torch.equal(c, c2)
+
+
+def test_error_paths_with_real_tensors():
+    B, L, D, N = 1, 64, 32, 16
+    prm = dev(I.make_params(D, N))
+    s = dev(I.make_sequence(B, L, D, N, "bf16"))
+    with pytest.raises(ssm.SsmError) as e:       # y aliases x
+        ssm.prefill(s["x"], s["dt"], s["z"], s["Bm"], s["Cm"], prm, y=s["x"])
+    assert e.value.status == 5
+    big = torch.empty(B * D * L + 8, dtype=torch.bfloat16, device=DEV)
+    x_mis = big[1:1 + B * D * L].view(B, D, L)   # 2-byte offset: misaligned
+    x_mis.copy_(s["x"])
+    with pytest.raises(ssm.SsmError) as e:
+        ssm.prefill(x_mis, s["dt"], s["z"], s["Bm"], s["Cm"], prm)
+    assert e.value.status == 4
