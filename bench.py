@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-SSM hot path on one MI355X.
+
+One step = one ssm_prefill over the workload's prompt (which leaves the h / conv cache)
+followed by its decode steps (one ssm_decode_step per token, each resuming from the cache).
+Inputs are synthetic and already resident in HBM when the timed region starts.
+
+Prints ONE JSON line: value = prefill Gelem/s over B*L*d_inner; decode_us_per_step is the
+mean decode-step time; roofline describes the prefill kernel; cpu_baseline is the fp64
+oracle timed on this host's cores on the same input bits.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD public specification
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, AMD public specification
+CONV_W = 4
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def flops_per_element(N: int) -> int:
+    """Algorithmic fp32 operations per (b, c, t) element, a transcendental counted as one:
+    conv 4 FMA (8); SiLU exp+add+rcp+mul (4); softplus add+exp+add+log (4); delta*u (1);
+    per state: delta*A, exp, (delta u)*B, FMA h, FMA y (7); D-skip FMA (2); gate (5)."""
+    return 8 + 4 + 4 + 1 + 7 * N + 2 + 5
+
+
+def prefill_bytes(B, L, D, N, es):
+    """Algorithmic HBM bytes of one prefill: read x, dt, z and write y once; B and C once;
+    final h and conv (fp32); per-channel parameters."""
+    return B * D * L * 4 * es + B * L * 2 * N * es + B * D * (N + CONV_W - 1) * 4 + D * (N + 7) * 4
+
+
+def decode_bytes(B, D, N, es):
+    """Algorithmic HBM bytes of one decode step: h and conv read + written (fp32), x, dt, z
+    read and y written, parameters, B_t and C_t."""
+    return B * D * (2 * (N + CONV_W - 1) * 4 + 4 * es) + D * (N + 7) * 4 + B * 2 * N * es
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_causal_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM traffic per prefill launch from the committed rocprofv3 --pmc summary, or None when
+    there is none for this workload or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, prm, seq_dev, toks_dev):
+    """Time the oracle (fp64, C, all host cores) on the same bits: the full prefill, then the
+    decode steps from its own cache."""
+    import oracle
+    import torch
+
+    cores = oracle.default_threads()
+    seq = {k: v.cpu() for k, v in seq_dev.items()}
+    t0 = time.perf_counter()
+    _, h, c = oracle.prefill(seq, prm, nthreads=cores)
+    t1 = time.perf_counter()
+    T = len(toks_dev)
+    toks = [{k: v.cpu() for k, v in t.items()} for t in toks_dev]
+    t2 = time.perf_counter()
+    for tok in toks:
+        _, h, c = oracle.decode_step(tok, prm, h, c, nthreads=cores)
+    t3 = time.perf_counter()
+    elems = w.batch * w.seqlen * w.d_inner
+    return {"value": round(elems / (t1 - t0) / 1e9, 4), "unit": "Gelem/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole prefill of the workload ({w.batch}x{w.seqlen}x{w.d_inner} elements) on the same bf16 "
+                      f"bits, then {T} decode steps from the oracle's own cache; threads over channels",
+            "prefill_s": round(t1 - t0, 3), "decode_us_per_step": round((t3 - t2) / max(T, 1) * 1e6, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="slice7b")
+    ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode step count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the channel-local recurrence would shard by channel with no exchange inside it).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import selective_state_space_causal_amd as ssm
+    from selective_state_space_causal_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    T = w.decode_steps if args.decode_steps is None else args.decode_steps
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ssm.load()
+    B, L, D, N = w.batch, w.seqlen, w.d_inner, w.d_state
+    es = 2 if w.io == "bf16" else 4
+    log(f"bench: {w.name} B={B} L={L} D={D} N={N} io={w.io} decode_steps={T}")
+
+    prm = I.make_params(D, N, dt_range=w.dt_range)
+    pd = {k: v.to(dev) for k, v in prm.items()}
+    seq = I.make_sequence_device(B, L, D, N, w.io, device=dev)
+    toks = [{k: v.to(dev) for k, v in I.make_decode_token(B, D, N, t, w.io).items()} for t in range(T)]
+    y = torch.empty_like(seq["x"])
+    h = torch.empty(B, D, N, dtype=torch.float32, device=dev)
+    c = torch.empty(B, D, CONV_W - 1, dtype=torch.float32, device=dev)
+    ys = torch.empty(max(T, 1), B, D, dtype=seq["x"].dtype, device=dev)
+    nws = ssm.workspace_bytes(B, L, D, N, seq["x"].dtype)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: copy calibration: 1 GiB read + 1 GiB written")
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(marks):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        ssm.prefill(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], pd, y=y, h_out=h, conv_out=c,
+                    workspace=ws, stream=stream)
+        e1.record(stream)
+        for t in range(T):
+            tk = toks[t]
+            ssm.decode_step(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, h, c, y_t=ys[t], stream=stream)
+        e2.record(stream)
+        marks.append((e0, e1, e2))
+
+    warm = []
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    marks = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(marks)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    pre_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / len(marks)
+    dec_ms = sum(b.elapsed_time(c_) for _, b, c_ in marks) / len(marks)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    elems = B * L * D
+    gelem = elems / (pre_ms * 1e-3) / 1e9
+    pbytes = prefill_bytes(B, L, D, N, es)
+    dbytes = decode_bytes(B, D, N, es)
+    p_gbps = pbytes / (pre_ms * 1e-3) / 1e9
+    d_us = dec_ms * 1e3 / max(T, 1)
+    d_gbps = dbytes / (d_us * 1e-6) / 1e9 if T else None
+    tflops = flops_per_element(N) * elems / (pre_ms * 1e-3) / 1e12
+    traffic = traffic_from_profiles(w.name)
+    log(f"bench: prefill {pre_ms:.3f} ms ({gelem:.1f} Gelem/s, {p_gbps:.0f} GB/s), decode {d_us:.2f} us/step")
+
+    rec = {
+        "metric": "prefill Gelem/s (B*L*d_inner) + decode us/step; % of HBM peak",
+        "value": round(gelem, 3), "unit": "Gelem/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N, "d_conv": CONV_W,
+                   "io": w.io, "state": "f32", "decode_steps": T, "parallelism": "none (one GPU's channel slice)"},
+        "prefill_ms": round(pre_ms, 4),
+        "decode_us_per_step": round(d_us, 3),
+        "prefill_hbm": {"achieved": round(p_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(p_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": pbytes},
+        "decode_hbm": None if not T else {"achieved": round(d_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                          "frac": round(d_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": dbytes},
+        "roofline": {"kernel": "prefill", "bound": "alu", "achieved": round(tflops, 3),
+                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+                     "flops_per_element": flops_per_element(N), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host cores")
+        rec["cpu_baseline"] = cpu_baseline(w, prm, seq, toks)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

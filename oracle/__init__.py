@@ -131,7 +131,7 @@ def prefill(seq: dict, params: dict, nthreads: int = 1, gate: bool = True):
                 params.get("conv_b"), nthreads=nthreads)
 
 
-def decode_step(tok: dict, params: dict, h, conv, gate: bool = True):
+def decode_step(tok: dict, params: dict, h, conv, gate: bool = True, nthreads: int = 1):
     """One decode step from the cache (h [B,D,N], conv [B,D,3]).
 
     ``tok`` holds x, dt, z as [B, D] and Bm, Cm as [B, N].  Returns
@@ -144,7 +144,7 @@ def decode_step(tok: dict, params: dict, h, conv, gate: bool = True):
                      _f64(tok["Bm"], np.shape(tok["Bm"]), "Bm")[:, None, :],
                      _f64(tok["Cm"], np.shape(tok["Cm"]), "Cm")[:, None, :],
                      params["A"], params["Dskip"], params["dt_bias"], params["conv_w"],
-                     params.get("conv_b"), h0=h, conv0=conv)
+                     params.get("conv_b"), h0=h, conv0=conv, nthreads=nthreads)
     return y[..., 0], h2, c2
 
 

@@ -32,8 +32,10 @@ struct ScanArgs {
 };
 
 // Prefill decompositions.
+// chunk_hint selects one explicitly; 0 lets choose_prefill_variant decide.
 enum PrefillVariant : int {
   kSequential = 1,  // one lane per (b, c) channel, tokens in order
+  kWindowed = 8,    // one wave per (b, c) channel, 8 tokens per lane, DPP scan across lanes
 };
 
 int choose_prefill_variant(const ScanArgs& a);

@@ -4,9 +4,16 @@
 namespace ssm {
 
 hipError_t launch_sequential(const ScanArgs& a, hipStream_t s);
+hipError_t launch_windowed(const ScanArgs& a, hipStream_t s);
+bool windowed_supported(const ScanArgs& a);
 
+// The windowed scan spreads each channel over a whole wave, so it fills the GPU even for one
+// batch row of a 2048-channel slice; it needs d_state == 16.  Everything else runs one lane per
+// channel.  The choice depends on d_state and chunk_hint only, never on the batch or channel
+// count, so a channel slice run alone reproduces the full run bit for bit.
 int choose_prefill_variant(const ScanArgs& a) {
-  (void)a;
+  if (a.chunk_hint == kSequential) return kSequential;
+  if (windowed_supported(a)) return kWindowed;
   return kSequential;
 }
 
@@ -18,6 +25,8 @@ size_t prefill_workspace_bytes(const ScanArgs& a) {
 hipError_t launch_prefill(const ScanArgs& a, void* workspace, hipStream_t s) {
   (void)workspace;
   switch (choose_prefill_variant(a)) {
+    case kWindowed:
+      return launch_windowed(a, s);
     default:
       return launch_sequential(a, s);
   }

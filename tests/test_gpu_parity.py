@@ -202,3 +202,41 @@ def test_error_paths_with_real_tensors():
     with pytest.raises(ssm.SsmError) as e:
         ssm.prefill(x_mis, s["dt"], s["z"], s["Bm"], s["Cm"], prm)
     assert e.value.status == 4
+
+
+WINDOWED = [
+    # B, L, D, io: aligned and ragged lengths, single-lane and single-window sequences,
+    # channel counts that leave idle waves in the last workgroup
+    (1, 8, 8, "bf16"), (1, 512, 16, "bf16"), (2, 520, 13, "bf16"), (1, 1024, 9, "f32"), (1, 4104, 24, "bf16"),
+    (3, 1536, 17, "f32"), (1, 2000, 8, "bf16"), (2, 7, 3, "f32"), (1, 1030, 31, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,L,D,io", WINDOWED)
+def test_windowed_kernel_shapes(B, L, D, io):
+    """The windowed (lanes over time) prefill, forced with chunk_hint=8, against the oracle."""
+    note(f"windowed B={B} L={L} D={D} {io}")
+    prm = I.make_params(D, 16, seed=L)
+    seq = I.make_sequence(B, L, D, 16, io, seed=L + 1)
+    check_full(seq, prm, io, what=f"windowed{B},{L},{D}", chunk_hint=8)
+    prm2 = dict(prm, conv_b=prm["conv_b"] - 0.05)
+    s = dev(seq)
+    h0 = torch.randn(B, D, 16, device=DEV)
+    c0 = torch.randn(B, D, 3, device=DEV)
+    y, h, c = ssm.prefill(s["x"], s["dt"], None, s["Bm"], s["Cm"], dev(prm2), h0=h0, conv0=c0, chunk_hint=8)
+    yr, hr, cr = oracle.scan(seq["x"], seq["dt"], None, seq["Bm"], seq["Cm"], prm2["A"], prm2["Dskip"],
+                             prm2["dt_bias"], prm2["conv_w"], prm2["conv_b"], h0=f64(h0), conv0=f64(c0))
+    assert_close(y, yr, TAU[io], "windowed resumed y")
+    assert_close(h, hr, TAU[io], "windowed resumed h")
+    assert_bitwise(c, cr, "windowed resumed conv")
+
+
+def test_windowed_and_sequential_agree():
+    B, L, D, N = 2, 3000, 40, 16
+    prm = I.make_params(D, N, seed=21)
+    seq = I.make_sequence(B, L, D, N, "f32", seed=21)
+    ya, ha, ca = run(seq, prm, chunk_hint=8)
+    yb, hb, cb = run(seq, prm, chunk_hint=1)
+    assert_close(ya, f64(yb), 1e-4, "windowed vs sequential y")
+    assert_close(ha, f64(hb), 1e-4, "windowed vs sequential h")
+    assert torch.equal(ca, cb)
