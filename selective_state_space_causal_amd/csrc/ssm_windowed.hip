@@ -117,97 +117,143 @@ struct Tile {
   float C[WAVE * LANE_STRIDE];
 };
 
-// K consecutive io values of one channel row starting at token t (zero past L).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw-buffer view of one tensor row: loads past `bytes` return zeros and stores past it are
+// dropped by the hardware, so ragged ends need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Unpack io words into fp32: bf16 pairs are (low, high) halves of a dword.
+template <typename IO>
+__device__ __forceinline__ float unpack(const uint32_t* w, int j) {
+  if constexpr (sizeof(IO) == 2)
+    return __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+  else
+    return __uint_as_float(w[j]);
+}
+
+template <typename IO>
+__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// K io values of a lane as dwords: 16-byte loads when rows are 16-byte aligned, element loads
+// otherwise; past the row end the buffer returns zeros.
 template <typename IO, bool ALIGNED>
-__device__ __forceinline__ void load_block(const IO* __restrict__ row, int64_t t, int64_t L, IO (&v)[K]) {
-  if (ALIGNED && t + K <= L) {
-    const uint4* p = reinterpret_cast<const uint4*>(row + t);
-    uint4 u[K * sizeof(IO) / 16];
+struct Lanes {
+  static constexpr int DW = K * (int)sizeof(IO) / 4;
+  uint32_t w[DW];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (ALIGNED) {
 #pragma unroll
-    for (int i = 0; i < (int)(K * sizeof(IO) / 16); ++i) u[i] = p[i];
-    __builtin_memcpy(v, u, sizeof(u));
+      for (int i = 0; i < DW; i += 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * i, soff, 0);
+        w[i] = v[0];
+        w[i + 1] = v[1];
+        w[i + 2] = v[2];
+        w[i + 3] = v[3];
+      }
+    } else if constexpr (sizeof(IO) == 2) {
+#pragma unroll
+      for (int i = 0; i < DW; ++i) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 4 * i, soff, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 4 * i + 2, soff, 0);
+        w[i] = lo | (hi << 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DW; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * i, soff, 0);
+    }
+  }
+};
+
+template <typename IO, bool ALIGNED>
+__device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&v)[K]) {
+  if constexpr (sizeof(IO) == 2) {
+    uint32_t w[K / 2];
+#pragma unroll
+    for (int i = 0; i < K / 2; ++i) w[i] = bf16_rne_bits<IO>(v[2 * i]) | (bf16_rne_bits<IO>(v[2 * i + 1]) << 16);
+    if constexpr (ALIGNED) {
+      const u32x4 v4 = {w[0], w[1], w[2], w[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(v4, r, voff, soff, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < K / 2; ++i) {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[i] & 0xFFFFu), r, voff + 4 * i, soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[i] >> 16), r, voff + 4 * i + 2, soff, 0);
+      }
+    }
   } else {
+    if constexpr (ALIGNED) {
 #pragma unroll
-    for (int j = 0; j < K; ++j) v[j] = (t + j < L) ? row[t + j] : IO{};
+      for (int i = 0; i < K; i += 4) {
+        const u32x4 v4 = {__float_as_uint(v[i]), __float_as_uint(v[i + 1]), __float_as_uint(v[i + 2]),
+                          __float_as_uint(v[i + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(v4, r, voff + 4 * i, soff, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < K; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), r, voff + 4 * i, soff, 0);
+    }
   }
 }
 
-template <typename IO, bool ALIGNED>
-__device__ __forceinline__ void store_block(IO* __restrict__ row, int64_t t, int64_t L, const IO (&v)[K]) {
-  if (ALIGNED && t + K <= L) {
-    uint4 u[K * sizeof(IO) / 16];
-    __builtin_memcpy(u, v, sizeof(u));
-    uint4* p = reinterpret_cast<uint4*>(row + t);
-#pragma unroll
-    for (int i = 0; i < (int)(K * sizeof(IO) / 16); ++i) p[i] = u[i];
-  } else {
-#pragma unroll
-    for (int j = 0; j < K; ++j)
-      if (t + j < L) row[t + j] = v[j];
-  }
-}
-
-// Window B / C staging: the tile of one io tensor is WIN * NS values, moved in 16-byte
-// chunks, PER_THREAD chunks per thread of the workgroup.
+// Window B / C staging: one io tensor's tile is WIN * NS values, moved as 16-byte chunks
+// (a batch row of B or C is L * 16 io values, a multiple of 16 bytes, so a chunk is either
+// wholly inside the row or wholly past its end and then reads as zeros).
 template <typename IO>
 struct TileChunks {
   static constexpr int EPC = 16 / sizeof(IO);          // io elements per chunk
   static constexpr int CHUNKS = WIN * NS / EPC;        // chunks per tensor per window
   static constexpr int PER_THREAD = CHUNKS / THREADS;
-  uint4 b[PER_THREAD], c[PER_THREAD];
+  uint32_t b[PER_THREAD][4], c[PER_THREAD][4];
+
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rc, int soff) {
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int voff = (threadIdx.x + r * THREADS) * 16;
+      const auto vb = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, soff, 0);
+      const auto vc = __builtin_amdgcn_raw_buffer_load_b128(rc, voff, soff, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        b[r][e] = vb[e];
+        c[r][e] = vc[e];
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(Tile& tile) const {
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int ci = threadIdx.x + r * THREADS;
+      const int token = ci * EPC / NS;
+      const int s0 = (ci * EPC) % NS;
+      const int off = (token / K) * LANE_STRIDE + (token % K) * NS + s0;
+#pragma unroll
+      for (int e = 0; e < EPC; e += 4) {
+        float4 fb, fc;
+        fb.x = unpack<IO>(b[r], e);
+        fb.y = unpack<IO>(b[r], e + 1);
+        fb.z = unpack<IO>(b[r], e + 2);
+        fb.w = unpack<IO>(b[r], e + 3);
+        fc.x = unpack<IO>(c[r], e);
+        fc.y = unpack<IO>(c[r], e + 1);
+        fc.z = unpack<IO>(c[r], e + 2);
+        fc.w = unpack<IO>(c[r], e + 3);
+        *reinterpret_cast<float4*>(&tile.B[off + e]) = fb;
+        *reinterpret_cast<float4*>(&tile.C[off + e]) = fc;
+      }
+    }
+  }
 };
-
-template <typename IO>
-__device__ __forceinline__ void tile_fetch(TileChunks<IO>& tc, const IO* __restrict__ Bm, const IO* __restrict__ Cm,
-                                           int64_t t0, int64_t L) {
-  using T = TileChunks<IO>;
-#pragma unroll
-  for (int r = 0; r < T::PER_THREAD; ++r) {
-    const int ci = threadIdx.x + r * THREADS;
-    const int token = ci * T::EPC / NS;
-    const int s0 = (ci * T::EPC) % NS;
-    const int64_t tt = t0 + token;
-    if (tt < L) {
-      tc.b[r] = *reinterpret_cast<const uint4*>(Bm + tt * NS + s0);
-      tc.c[r] = *reinterpret_cast<const uint4*>(Cm + tt * NS + s0);
-    } else {
-      tc.b[r] = make_uint4(0, 0, 0, 0);
-      tc.c[r] = make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-template <typename IO>
-__device__ __forceinline__ void widen(const uint4& u, float (&f)[16 / sizeof(IO)]) {
-  IO v[16 / sizeof(IO)];
-  __builtin_memcpy(v, &u, 16);
-#pragma unroll
-  for (int e = 0; e < (int)(16 / sizeof(IO)); ++e) f[e] = to_f32(v[e]);
-}
-
-template <typename IO>
-__device__ __forceinline__ void tile_store(Tile& tile, const TileChunks<IO>& tc) {
-  using T = TileChunks<IO>;
-#pragma unroll
-  for (int r = 0; r < T::PER_THREAD; ++r) {
-    const int ci = threadIdx.x + r * THREADS;
-    const int token = ci * T::EPC / NS;
-    const int s0 = (ci * T::EPC) % NS;
-    const int off = (token / K) * LANE_STRIDE + (token % K) * NS + s0;
-    float fb[T::EPC], fc[T::EPC];
-    widen<IO>(tc.b[r], fb);
-    widen<IO>(tc.c[r], fc);
-#pragma unroll
-    for (int e = 0; e < T::EPC; e += 4) {
-      *reinterpret_cast<float4*>(&tile.B[off + e]) = make_float4(fb[e], fb[e + 1], fb[e + 2], fb[e + 3]);
-      *reinterpret_cast<float4*>(&tile.C[off + e]) = make_float4(fc[e], fc[e + 1], fc[e + 2], fc[e + 3]);
-    }
-  }
-}
 
 template <typename IO, bool ALIGNED>
 __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
   __shared__ Tile tile;
+  constexpr int ES = sizeof(IO);
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
   const int64_t groups = (a.D + W - 1) / W;
@@ -215,17 +261,19 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
   const int64_t c = (blockIdx.x - b * groups) * W + wave;
   const bool active = c < a.D;  // a ragged last group: idle waves still stage tiles and meet barriers
   const int64_t L = a.L;
-  const int64_t row = b * a.D + (active ? c : 0);
+  const int64_t cc = active ? c : 0;
+  const int64_t row = b * a.D + cc;
+  const int64_t row_bytes = L * ES;
 
-  const IO* __restrict__ Bm = static_cast<const IO*>(a.Bm) + b * L * NS;
-  const IO* __restrict__ Cm = static_cast<const IO*>(a.Cm) + b * L * NS;
-  const IO* __restrict__ xr = static_cast<const IO*>(a.x) + row * L;
-  const IO* __restrict__ dtr = static_cast<const IO*>(a.dt) + row * L;
-  const IO* __restrict__ zr = a.z ? static_cast<const IO*>(a.z) + row * L : nullptr;
-  IO* __restrict__ yr = static_cast<IO*>(a.y) + row * L;
+  const auto rx = row_rsrc(static_cast<const IO*>(a.x) + row * L, row_bytes);
+  const auto rdt = row_rsrc(static_cast<const IO*>(a.dt) + row * L, row_bytes);
+  const auto rz = row_rsrc(a.z ? static_cast<const IO*>(a.z) + row * L : a.x, a.z ? row_bytes : 0);
+  const auto ry = row_rsrc(static_cast<IO*>(a.y) + row * L, active ? row_bytes : 0);
+  const auto rB = row_rsrc(static_cast<const IO*>(a.Bm) + b * L * NS, L * NS * ES);
+  const auto rC = row_rsrc(static_cast<const IO*>(a.Cm) + b * L * NS, L * NS * ES);
+  const bool gate = a.z != nullptr;
 
   // Channel constants.
-  const int64_t cc = active ? c : 0;
   const float w0 = a.conv_w[cc * 4 + 0], w1 = a.conv_w[cc * 4 + 1], w2 = a.conv_w[cc * 4 + 2],
               w3 = a.conv_w[cc * 4 + 3];
   const float cb = a.conv_b ? a.conv_b[cc] : 0.0f;
@@ -244,41 +292,34 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
   }
   const float init0 = hist0, init1 = hist1, init2 = hist2;
 
-  const int64_t nwin = (L + WIN - 1) / WIN;
+  const int nwin = (int)((L + WIN - 1) / WIN);
+  const int voff = lane * K * ES;  // this lane's byte offset inside a window
   TileChunks<IO> pf;
-  IO px[K], pdt[K], pz[K];
-#pragma unroll
-  for (int j = 0; j < K; ++j) pz[j] = IO{};
-  tile_fetch<IO>(pf, Bm, Cm, 0, L);
-  load_block<IO, ALIGNED>(xr, (int64_t)lane * K, L, px);
-  load_block<IO, ALIGNED>(dtr, (int64_t)lane * K, L, pdt);
-  if (zr) load_block<IO, ALIGNED>(zr, (int64_t)lane * K, L, pz);
+  Lanes<IO, ALIGNED> px, pdt, pz;
+  pf.fetch(rB, rC, 0);
+  px.load(rx, voff, 0);
+  pdt.load(rdt, voff, 0);
+  if (gate) pz.load(rz, voff, 0);
 
-  for (int64_t w = 0; w < nwin; ++w) {
-    const int64_t t0 = w * WIN;
-    const int64_t tl = t0 + (int64_t)lane * K;  // this lane's first token
+  for (int w = 0; w < nwin; ++w) {
+    const int t0 = w * WIN;
     __syncthreads();  // every wave is done reading the previous tile
-    tile_store<IO>(tile, pf);
+    pf.store(tile);
     __syncthreads();
-    IO cx[K], cdt[K], cz[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      cx[j] = px[j];
-      cdt[j] = pdt[j];
-      cz[j] = pz[j];
-    }
+    const Lanes<IO, ALIGNED> cx = px, cdt = pdt, cz = pz;
     if (w + 1 < nwin) {  // prefetch the next window while this one is computed
-      tile_fetch<IO>(pf, Bm, Cm, t0 + WIN, L);
-      load_block<IO, ALIGNED>(xr, tl + WIN, L, px);
-      load_block<IO, ALIGNED>(dtr, tl + WIN, L, pdt);
-      if (zr) load_block<IO, ALIGNED>(zr, tl + WIN, L, pz);
+      pf.fetch(rB, rC, (t0 + WIN) * NS * ES);
+      px.load(rx, voff, (t0 + WIN) * ES);
+      pdt.load(rdt, voff, (t0 + WIN) * ES);
+      if (gate) pz.load(rz, voff, (t0 + WIN) * ES);
     }
     if (!active) continue;
 
-    // ---- front end: conv window, SiLU, softplus, gate ----
+    // ---- front end: conv window, SiLU, softplus ----
+    const int nvalid = (int)min<int64_t>(max<int64_t>(L - t0 - (int64_t)lane * K, 0), K);
     float xv[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) xv[j] = to_f32(cx[j]);
+    for (int j = 0; j < K; ++j) xv[j] = unpack<IO>(cx.w, j);
     const float xm3 = dpp<DPP_WAVE_SHR1, 0xf>(hist0, xv[K - 3]);
     const float xm2 = dpp<DPP_WAVE_SHR1, 0xf>(hist1, xv[K - 2]);
     const float xm1 = dpp<DPP_WAVE_SHR1, 0xf>(hist2, xv[K - 1]);
@@ -286,21 +327,19 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
     hist1 = lane63(xv[K - 2]);
     hist2 = lane63(xv[K - 1]);
 
-    float dl[K], du[K], yv[K], gt[K];
+    float dl[K], du[K], yv[K];
     float dsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const float s3 = j >= 3 ? xv[j - 3] : (j == 0 ? xm3 : (j == 1 ? xm2 : xm1));
       const float s2 = j >= 2 ? xv[j - 2] : (j == 0 ? xm2 : xm1);
       const float s1 = j >= 1 ? xv[j - 1] : xm1;
-      const float v = cb + w0 * s3 + w1 * s2 + w2 * s1 + w3 * xv[j];
+      const float v = fmaf(w3, xv[j], fmaf(w2, s1, fmaf(w1, s2, fmaf(w0, s3, cb))));
       const float u = silu(v);
-      const bool valid = tl + j < L;
-      const float d = valid ? softplus(to_f32(cdt[j]) + dtb) : 0.0f;  // delta = 0: identity step
+      const float d = j < nvalid ? softplus(unpack<IO>(cdt.w, j) + dtb) : 0.0f;  // 0: identity step
       dl[j] = d;
       du[j] = d * u;
       yv[j] = dsk * u;
-      gt[j] = zr ? silu(to_f32(cz[j])) : 1.0f;
       dsum += d;
     }
 
@@ -344,16 +383,18 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
       }
     }
 
-    IO out[K];
+    if (gate) {
 #pragma unroll
-    for (int j = 0; j < K; ++j) out[j] = from_f32<IO>(yv[j] * gt[j]);
-    store_block<IO, ALIGNED>(yr, tl, L, out);
+      for (int j = 0; j < K; ++j) yv[j] *= silu(unpack<IO>(cz.w, j));
+    }
+    store_lanes<IO, ALIGNED>(ry, voff, t0 * ES, yv);
   }
 
   if (active && lane == 0) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) a.h_out[row * NS + n] = carry[n];
     const float init[3] = {init0, init1, init2};
+    const IO* xr = static_cast<const IO*>(a.x) + row * L;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const int64_t t = L - 3 + j;  // raw input xi[L-3+j]; history below zero
@@ -364,7 +405,11 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
 
 }  // namespace
 
-bool windowed_supported(const ScanArgs& a) { return a.N == NS; }
+// Buffer offsets are 32-bit: a batch row of B / C (L * 16 io values) must stay below 2 GiB.
+bool windowed_supported(const ScanArgs& a) {
+  const int64_t es = a.bf16 ? 2 : 4;
+  return a.N == NS && a.L * NS * es < ((int64_t)1 << 31) - WIN * NS * es;
+}
 
 hipError_t launch_windowed(const ScanArgs& a, hipStream_t s) {
   const int64_t groups = (a.D + W - 1) / W;
