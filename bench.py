@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--workload", default="slice7b")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode step count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager-decode", action="store_true", help="time decode as one host call per step "
+                    "instead of replaying the captured HIP graph")
+    ap.add_argument("--chunk-hint", type=int, default=0, help="prefill decomposition (0 auto, 1 sequential, 8 windowed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -150,15 +153,36 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
+    def decode_loop(s=None):
+        for t in range(T):
+            tk = toks[t]
+            ssm.decode_step(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, h, c, y_t=ys[t], stream=s)
+
+    # The decode loop as a serving loop runs it: captured once in a HIP graph, replayed per
+    # request.  (An eager, one-launch-per-call loop is timed separately below.)
+    graph = None
+    if T and not args.eager_decode:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            decode_loop()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_loop()
+        torch.cuda.synchronize()
+
     def step(marks):
         e0, e1, e2 = ev(), ev(), ev()
         e0.record(stream)
         ssm.prefill(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], pd, y=y, h_out=h, conv_out=c,
-                    workspace=ws, stream=stream)
+                    workspace=ws, stream=stream, chunk_hint=args.chunk_hint)
         e1.record(stream)
-        for t in range(T):
-            tk = toks[t]
-            ssm.decode_step(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, h, c, y_t=ys[t], stream=stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            decode_loop(stream)
         e2.record(stream)
         marks.append((e0, e1, e2))
 
@@ -173,6 +197,17 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
+    eager_us = None
+    if T:  # eager decode loop (one host call per step), for reference
+        e0, e1 = ev(), ev()
+        decode_loop(stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        decode_loop(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / T
+
     pre_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / len(marks)
     dec_ms = sum(b.elapsed_time(c_) for _, b, c_ in marks) / len(marks)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -181,11 +216,13 @@ def main():
     pbytes = prefill_bytes(B, L, D, N, es)
     dbytes = decode_bytes(B, D, N, es)
     p_gbps = pbytes / (pre_ms * 1e-3) / 1e9
-    d_us = dec_ms * 1e3 / max(T, 1)
+    d_us = dec_ms * 1e3 / T if T else None
     d_gbps = dbytes / (d_us * 1e-6) / 1e9 if T else None
     tflops = flops_per_element(N) * elems / (pre_ms * 1e-3) / 1e12
     traffic = traffic_from_profiles(w.name)
-    log(f"bench: prefill {pre_ms:.3f} ms ({gelem:.1f} Gelem/s, {p_gbps:.0f} GB/s), decode {d_us:.2f} us/step")
+    log(f"bench: prefill {pre_ms:.3f} ms ({gelem:.1f} Gelem/s, {p_gbps:.0f} GB/s)" +
+        (f", decode {d_us:.2f} us/step ({'graph' if graph is not None else 'eager'}; eager {eager_us:.2f} us/step)"
+         if T else ""))
 
     rec = {
         "metric": "prefill Gelem/s (B*L*d_inner) + decode us/step; % of HBM peak",
@@ -195,7 +232,9 @@ def main():
         "config": {"workload": w.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N, "d_conv": CONV_W,
                    "io": w.io, "state": "f32", "decode_steps": T, "parallelism": "none (one GPU's channel slice)"},
         "prefill_ms": round(pre_ms, 4),
-        "decode_us_per_step": round(d_us, 3),
+        "decode_us_per_step": None if d_us is None else round(d_us, 3),
+        "decode_mode": "hip_graph" if graph is not None else "eager",
+        "decode_us_per_step_eager": None if eager_us is None else round(eager_us, 3),
         "prefill_hbm": {"achieved": round(p_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(p_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": pbytes},
         "decode_hbm": None if not T else {"achieved": round(d_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

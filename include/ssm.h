@@ -44,7 +44,9 @@
  *              invalid call returns a non-zero ssm_status and enqueues nothing.
  *              A launch failure returns SSM_ERR_LAUNCH.  No exception crosses
  *              the ABI.  Non-finite inputs are outside the contract.
- *   Alignment  every tensor base pointer must be 16-byte aligned.
+ *   Alignment  prefill: every tensor base pointer 16-byte aligned.  Decode step: io
+ *              tensors naturally aligned (2 bytes bf16, 4 bytes fp32), h 16-byte, the conv
+ *              window 4-byte.  Parameters (both): A and conv_w 16-byte, the rest 4-byte.
  *   Aliasing   outputs may not overlap inputs or each other, except that the
  *              decode step updates h and conv in place by design.
  *   Device     kernels run on the calling thread's current HIP device.
@@ -68,7 +70,7 @@ typedef enum {
   SSM_ERR_NULL = 1,      /* a required pointer is NULL */
   SSM_ERR_SHAPE = 2,     /* a size is < 1, d_state > 16, d_conv != 4, or sizes overflow */
   SSM_ERR_DTYPE = 3,     /* io_dtype is not SSM_F32 or SSM_BF16 */
-  SSM_ERR_ALIGN = 4,     /* a tensor base pointer is not 16-byte aligned */
+  SSM_ERR_ALIGN = 4,     /* a tensor base pointer breaks the alignment rule below */
   SSM_ERR_ALIAS = 5,     /* an output overlaps an input or another output */
   SSM_ERR_WORKSPACE = 6, /* workspace NULL or smaller than ssm_prefill_workspace_bytes() */
   SSM_ERR_LAUNCH = 7     /* a kernel launch failed (hipGetLastError) */
@@ -84,9 +86,12 @@ typedef struct {
   int64_t d_state;  /* N in [1, 16] */
   int64_t d_conv;   /* must be 4 */
   int32_t io_dtype; /* ssm_dtype of x, dt, z, Bm, Cm and y */
-  int32_t chunk_hint; /* prefill decomposition: 0 = automatic; a positive value forces the
-                         kernel variant and the per-lane token count so results do not depend
-                         on the batch or channel count (see ssm_prefill) */
+  int32_t chunk_hint; /* prefill decomposition: 0 = automatic, 1 = one lane per channel walking
+                         its tokens in order, 8 = one wave per channel with 8 tokens per lane
+                         (d_state 16 only; otherwise the one-lane form runs).  Any other value
+                         is SSM_ERR_SHAPE.  The automatic choice depends on d_state and L only,
+                         never on batch or d_inner, so a channel slice run alone reproduces the
+                         full run bit for bit. */
 } ssm_dims;
 
 /* Per-channel parameters, device fp32.  conv_b may be NULL (zero bias). */

@@ -26,13 +26,15 @@ Range span(const void* p, int64_t bytes) {
 
 bool overlaps(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
 
 // Shape / dtype checks shared by both entry points.  L is validated only when use_L.
 int check_dims(const ssm_dims* d, bool use_L) {
   if (!d) return SSM_ERR_NULL;
   if (d->batch < 1 || d->d_inner < 1 || d->d_state < 1 || d->d_state > SSM_MAX_STATE ||
-      d->d_conv != SSM_CONV_WIDTH || (use_L && d->seqlen < 1) || d->chunk_hint < 0)
+      d->d_conv != SSM_CONV_WIDTH || (use_L && d->seqlen < 1) ||
+      (use_L && d->chunk_hint != 0 && d->chunk_hint != 1 && d->chunk_hint != 8))
     return SSM_ERR_SHAPE;
   if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   // Every byte count the kernels index must fit comfortably in int64.
@@ -49,9 +51,10 @@ int check_params(const ssm_params* p, const void* const* outs, const int64_t* ou
   if (!p || !p->A || !p->Dskip || !p->dt_bias || !p->conv_w) return SSM_ERR_NULL;
   const void* ptrs[5] = {p->A, p->Dskip, p->dt_bias, p->conv_w, p->conv_b};
   const int64_t bytes[5] = {D * N * 4, D * 4, D * 4, D * 4 * 4, D * 4};
+  const uintptr_t align[5] = {16, 4, 4, 16, 4};  // A and conv_w rows are read as 16-byte vectors
   for (int i = 0; i < 5; ++i) {
     if (!ptrs[i]) continue;
-    if (!aligned16(ptrs[i])) return SSM_ERR_ALIGN;
+    if (!aligned(ptrs[i], align[i])) return SSM_ERR_ALIGN;
     for (int o = 0; o < nouts; ++o)
       if (overlaps(span(ptrs[i], bytes[i]), span(outs[o], out_bytes[o]))) return SSM_ERR_ALIAS;
   }
@@ -87,7 +90,7 @@ const char* ssm_status_str(int s) {
     case SSM_ERR_NULL: return "a required pointer is NULL";
     case SSM_ERR_SHAPE: return "invalid sizes (batch/seqlen/d_inner >= 1, 1 <= d_state <= 16, d_conv == 4)";
     case SSM_ERR_DTYPE: return "io_dtype must be SSM_F32 or SSM_BF16";
-    case SSM_ERR_ALIGN: return "tensor base pointers must be 16-byte aligned";
+    case SSM_ERR_ALIGN: return "a tensor base pointer is misaligned (see the alignment rule in ssm.h)";
     case SSM_ERR_ALIAS: return "an output overlaps an input or another output";
     case SSM_ERR_WORKSPACE: return "workspace missing or smaller than ssm_prefill_workspace_bytes()";
     case SSM_ERR_LAUNCH: return "kernel launch failed";
@@ -167,10 +170,11 @@ int ssm_decode_step(const ssm_dims* d, const ssm_params* p, const void* x_t, con
   const int64_t in_bytes[5] = {tok, tok, tok, bc, bc};
   const void* outs[3] = {y_t, h, conv_state};
   const int64_t out_bytes[3] = {tok, hb, cvb};
+  // Decode reads io tensors element by element: natural alignment suffices.  h moves as
+  // 16-byte vectors; the conv window as floats.
   for (int i = 0; i < 5; ++i)
-    if (ins[i] && !aligned16(ins[i])) return SSM_ERR_ALIGN;
-  for (int o = 0; o < 3; ++o)
-    if (!aligned16(outs[o])) return SSM_ERR_ALIGN;
+    if (ins[i] && !aligned(ins[i], (uintptr_t)es)) return SSM_ERR_ALIGN;
+  if (!aligned(y_t, (uintptr_t)es) || !aligned16(h) || !aligned(conv_state, 4)) return SSM_ERR_ALIGN;
   st = check_params(p, outs, out_bytes, 3, D, N);
   if (st != SSM_OK) return st;
   for (int o = 0; o < 3; ++o) {

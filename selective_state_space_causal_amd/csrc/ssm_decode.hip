@@ -1,0 +1,87 @@
+// ssm_decode.hip -- decode step: one new token per batch row, resumed from the cached state
+// ("Scaling State-Space Models on Multiple GPUs with Tensor Parallelism", euno.news summary
+// of arXiv 2602.21144, Methodology item 3: the state left by prefill is reused token by token).
+//
+// Four lanes share one (b, c) channel; lane q of the quad owns states 4q .. 4q+3, so each
+// lane moves its slice of h with one 16-byte load and one 16-byte store (consecutive lanes,
+// consecutive addresses).  Every lane of the quad evaluates the channel's front end (conv
+// window, SiLU, softplus, gate) on the same broadcast inputs; the readout C_t . h_t is
+// summed over the quad with two DPP adds.  Lane 0 of the quad writes y_t and the shifted
+// conv window.  Each quad owns its channel's cache entries, so the in-place update is
+// race-free.
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+constexpr int QS = 4;  // states per lane
+
+__device__ __forceinline__ float quad_sum(float v) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad ends with the quad's total.
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  return v;
+}
+
+template <typename IO>
+__global__ __launch_bounds__(256) void decode_quad(ScanArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t rows = a.B * a.D;
+  const int64_t row = min(gid >> 2, rows - 1);  // a ragged tail repeats the last channel, writes nothing
+  const bool live = (gid >> 2) < rows;
+  const int q = (int)(gid & 3);
+  const int64_t b = row / a.D, c = row - b * a.D;
+
+  const float4 w = *reinterpret_cast<const float4*>(a.conv_w + c * 4);
+  const float cb = a.conv_b ? a.conv_b[c] : 0.0f;
+  const float dtb = a.dt_bias[c], dsk = a.Dskip[c];
+  const float4 A4 = *reinterpret_cast<const float4*>(a.A + c * 16 + q * QS);
+  const float4 h4 = *reinterpret_cast<const float4*>(a.h0 + row * 16 + q * QS);
+  const float* cv = a.conv0 + row * 3;
+  const float x0 = cv[0], x1 = cv[1], x2 = cv[2];
+  const IO* Bt = static_cast<const IO*>(a.Bm) + b * 16 + q * QS;
+  const IO* Ct = static_cast<const IO*>(a.Cm) + b * 16 + q * QS;
+  const float xt = to_f32(static_cast<const IO*>(a.x)[row]);
+  const float dtr = to_f32(static_cast<const IO*>(a.dt)[row]);
+
+  const float v = cb + w.x * x0 + w.y * x1 + w.z * x2 + w.w * xt;
+  const float u = silu(v);
+  const float delta = softplus(dtr + dtb);
+  const float du = delta * u;
+  const float Aq[QS] = {A4.x, A4.y, A4.z, A4.w};
+  float h[QS] = {h4.x, h4.y, h4.z, h4.w};
+  float r = 0.0f;
+#pragma unroll
+  for (int n = 0; n < QS; ++n) {
+    const float dA = hw_exp2(delta * (Aq[n] * kLog2e));
+    h[n] = fmaf(dA, h[n], du * to_f32(Bt[n]));
+    r = fmaf(to_f32(Ct[n]), h[n], r);
+  }
+  r = quad_sum(r);
+  r = fmaf(dsk, u, r);
+  if (a.z) r *= silu(to_f32(static_cast<const IO*>(a.z)[row]));
+  if (!live) return;
+  *reinterpret_cast<float4*>(a.h_out + row * 16 + q * QS) = make_float4(h[0], h[1], h[2], h[3]);
+  if (q == 0) {
+    static_cast<IO*>(a.y)[row] = from_f32<IO>(r);
+    float* co = a.conv_out + row * 3;
+    co[0] = x1;
+    co[1] = x2;
+    co[2] = xt;
+  }
+}
+
+}  // namespace
+
+bool decode_quad_supported(const ScanArgs& a) { return a.N == 16; }
+
+hipError_t launch_decode_quad(const ScanArgs& a, hipStream_t s) {
+  const int64_t lanes = a.B * a.D * 4;
+  const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+  if (a.bf16) decode_quad<bf16_t><<<grid, block, 0, s>>>(a);
+  else decode_quad<float><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -139,7 +139,11 @@ hipError_t launch_sequential(const ScanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+bool decode_quad_supported(const ScanArgs& a);
+hipError_t launch_decode_quad(const ScanArgs& a, hipStream_t s);
+
 hipError_t launch_decode(const ScanArgs& a, hipStream_t s) {
+  if (decode_quad_supported(a)) return launch_decode_quad(a, s);
   const dim3 grid = rows_grid(a), block(256);
   if (a.bf16) {
     if (a.N == 16) decode_step<bf16_t, 16, true><<<grid, block, 0, s>>>(a);

@@ -87,7 +87,7 @@ NULL, SHAPE, DTYPE, ALIGN, ALIAS, WS = 1, 2, 3, 4, 5, 6
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), SHAPE), (dict(seqlen=0), SHAPE), (dict(d_inner=-1), SHAPE), (dict(d_state=0), SHAPE),
-    (dict(d_state=17), SHAPE), (dict(d_conv=3), SHAPE), (dict(chunk_hint=-2), SHAPE),
+    (dict(d_state=17), SHAPE), (dict(d_conv=3), SHAPE), (dict(chunk_hint=-2), SHAPE), (dict(chunk_hint=3), SHAPE),
     (dict(batch=1 << 40, d_inner=1 << 30), SHAPE), (dict(io_dtype=7), DTYPE)])
 def test_prefill_rejects_bad_dims(kw, code):
     assert prefill(dims(**kw), params()) == code
@@ -106,7 +106,9 @@ def test_prefill_alignment():
     for k in ("x", "dt", "z", "Bm", "Cm", "y", "h_out", "conv_out"):
         assert prefill(dims(), params(), **{k: fake(0 if k != "x" else 9, 8)}) == ALIGN, k
     assert prefill(dims(), params(), h0=fake(10, 4)) == ALIGN
-    assert prefill(dims(), params(conv_b=BASE + 24 * STEP + 4)) == ALIGN
+    assert prefill(dims(), params(conv_b=BASE + 24 * STEP + 2)) == ALIGN
+    assert prefill(dims(), params(A=BASE + 20 * STEP + 4)) == ALIGN
+    assert prefill(dims(), params(conv_w=BASE + 23 * STEP + 8)) == ALIGN
 
 
 def test_prefill_aliasing():
@@ -128,6 +130,9 @@ def test_decode_validation():
     for k in ("x", "dt", "Bt", "Ct", "y", "h", "conv"):
         assert decode(dims(), params(), **{k: None}) == NULL, k
     assert decode(dims(), params(), h=fake(6, 4)) == ALIGN
+    assert decode(dims(), params(), x=fake(0, 1)) == ALIGN            # bf16 needs 2-byte alignment
+    assert decode(dims(), params(), conv=fake(7, 2)) == ALIGN
+    assert decode(dims(io_dtype=L.SSM_F32), params(), y=fake(5, 2)) == ALIGN
     assert decode(dims(), params(), y=fake(0)) == ALIAS            # y_t over x_t
     assert decode(dims(), params(), conv=fake(6, 256)) == ALIAS    # conv inside h
     assert decode(dims(), params(), h=ctypes.c_void_p(BASE + 23 * STEP)) == ALIAS   # h over conv_w
