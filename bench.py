@@ -72,6 +72,58 @@ def traffic_from_profiles(workload):
     return rec.get("bytes_per_launch")
 
 
+PMC_COMMAND = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} -d $REPO/gpurun_out/pmc -o {ctr} "
+               "--output-format csv -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline "
+               "--decode-steps 8 --copy-calibration --workload {workload}")
+
+
+def record_traffic(pmc_dir, workload):
+    """Turn the two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into
+    profiles/traffic.json.  Each counter is scaled by what it reads for the plain 1 GiB copy
+    run in the same process (--copy-calibration): 1 GiB read and 1 GiB written."""
+    import csv
+    from collections import defaultdict
+
+    per = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = list(csv.DictReader(open(os.path.join(pmc_dir, f"{ctr}_counter_collection.csv"))))
+        vals = defaultdict(list)
+        for r in rows:
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        per[ctr] = vals
+    gib_kib = float(1 << 20)
+    # the calibration copy is the only dispatch that writes a full GiB
+    copy_name = max(per["WRITE_SIZE"], key=lambda k: max(per["WRITE_SIZE"][k]))
+    wi = per["WRITE_SIZE"][copy_name].index(max(per["WRITE_SIZE"][copy_name]))
+    fetch_scale = gib_kib / per["FETCH_SIZE"][copy_name][wi]
+    write_scale = gib_kib / per["WRITE_SIZE"][copy_name][wi]
+
+    def kernel(tag):
+        names = [k for k in per["FETCH_SIZE"] if tag in k]
+        if not names:
+            return None
+        k = names[0]
+        f = sum(per["FETCH_SIZE"][k]) / len(per["FETCH_SIZE"][k])
+        w = sum(per["WRITE_SIZE"][k]) / len(per["WRITE_SIZE"][k])
+        return {"kernel": k, "dispatches": len(per["FETCH_SIZE"][k]), "fetch_kib_raw": round(f, 1),
+                "write_kib_raw": round(w, 1), "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+                "bytes_per_launch": int(round((f * fetch_scale + w * write_scale) * 1024))}
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    entry = {"source_hash": kernel_source_hash(), "command": PMC_COMMAND.format(ctr="<FETCH_SIZE|WRITE_SIZE>",
+                                                                                 workload=workload),
+             "copy_calibration": {"kernel": copy_name, "fetch_scale": round(fetch_scale, 4),
+                                  "write_scale": round(write_scale, 4)},
+             "prefill": kernel("prefill_"), "decode": kernel("decode_")}
+    entry["bytes_per_launch"] = entry["prefill"]["bytes_per_launch"] if entry["prefill"] else None
+    rec[workload] = entry
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(entry, indent=1))
+
+
 def cpu_baseline(w, prm, seq_dev, toks_dev):
     """Time the oracle (fp64, C, all host cores) on the same bits: the full prefill, then the
     decode steps from its own cache."""
@@ -109,7 +161,12 @@ def main():
     ap.add_argument("--chunk-hint", type=int, default=0, help="prefill decomposition (0 auto, 1 sequential, 8 windowed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--record-traffic", metavar="PMC_DIR", default=None,
+                    help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs and exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic, args.workload)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
