@@ -134,10 +134,11 @@ __device__ __forceinline__ float unpack(const uint32_t* w, int j) {
     return __uint_as_float(w[j]);
 }
 
-template <typename IO>
-__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 values -> two bf16 (round to nearest even) packed in a dword, first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
 
 // K io values of a lane as dwords: 16-byte loads when rows are 16-byte aligned, element loads
@@ -175,7 +176,7 @@ __device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, 
   if constexpr (sizeof(IO) == 2) {
     uint32_t w[K / 2];
 #pragma unroll
-    for (int i = 0; i < K / 2; ++i) w[i] = bf16_rne_bits<IO>(v[2 * i]) | (bf16_rne_bits<IO>(v[2 * i + 1]) << 16);
+    for (int i = 0; i < K / 2; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     if constexpr (ALIGNED) {
       const u32x4 v4 = {w[0], w[1], w[2], w[3]};
       __builtin_amdgcn_raw_buffer_store_b128(v4, r, voff, soff, 0);

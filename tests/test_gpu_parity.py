@@ -240,3 +240,24 @@ def test_windowed_and_sequential_agree():
     assert_close(ya, f64(yb), 1e-4, "windowed vs sequential y")
     assert_close(ha, f64(hb), 1e-4, "windowed vs sequential h")
     assert torch.equal(ca, cb)
+
+
+@pytest.mark.parametrize("L,D", [(1024, 24), (777, 9)])
+def test_bf16_output_is_rne_of_fp32_output(L, D):
+    """Same bf16-representable inputs through the fp32-io and bf16-io paths: the arithmetic is
+    identical, so the bf16 outputs must be the round-to-nearest-even of the fp32 outputs (bit for
+    bit) and the fp32 state identical -- for prefill and for a decode step."""
+    B, N = 2, 16
+    prm = dev(I.make_params(D, N, seed=41))
+    s16 = dev(I.make_sequence(B, L, D, N, "bf16", seed=41))
+    s32 = {k: v.float() for k, v in s16.items()}
+    y16, h16, c16 = ssm.prefill(s16["x"], s16["dt"], s16["z"], s16["Bm"], s16["Cm"], prm)
+    y32, h32, c32 = ssm.prefill(s32["x"], s32["dt"], s32["z"], s32["Bm"], s32["Cm"], prm)
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(h16, h32) and torch.equal(c16, c32)
+    t16 = dev(I.make_decode_token(B, D, N, 0, "bf16", seed=41))
+    t32 = {k: v.float() for k, v in t16.items()}
+    u16 = ssm.decode_step(t16["x"], t16["dt"], t16["z"], t16["Bm"], t16["Cm"], prm, h16, c16)
+    u32 = ssm.decode_step(t32["x"], t32["dt"], t32["z"], t32["Bm"], t32["Cm"], prm, h32, c32)
+    assert torch.equal(u16.view(torch.int16), u32.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(h16, h32) and torch.equal(c16, c32)
