@@ -253,7 +253,7 @@ struct TileChunks {
 
 template <typename IO, bool ALIGNED>
 __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
-  __shared__ Tile tile;
+  __shared__ Tile tiles[2];  // window w reads tiles[w & 1] while window w + 1's goes into the other
   constexpr int ES = sizeof(IO);
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
@@ -302,19 +302,25 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
   pdt.load(rdt, voff, 0);
   if (gate) pz.load(rz, voff, 0);
 
+  pf.store(tiles[0]);
   for (int w = 0; w < nwin; ++w) {
     const int t0 = w * WIN;
-    __syncthreads();  // every wave is done reading the previous tile
-    pf.store(tile);
+    // One barrier per window: window w's tile (written at the end of window w-1) is visible,
+    // and every wave is done reading tiles[(w+1) & 1] (window w-1's), which is refilled below.
     __syncthreads();
+    const Tile& tile = tiles[w & 1];
     const Lanes<IO, ALIGNED> cx = px, cdt = pdt, cz = pz;
-    if (w + 1 < nwin) {  // prefetch the next window while this one is computed
+    const bool more = w + 1 < nwin;
+    if (more) {  // prefetch the next window while this one is computed
       pf.fetch(rB, rC, (t0 + WIN) * NS * ES);
       px.load(rx, voff, (t0 + WIN) * ES);
       pdt.load(rdt, voff, (t0 + WIN) * ES);
       if (gate) pz.load(rz, voff, (t0 + WIN) * ES);
     }
-    if (!active) continue;
+    if (!active) {
+      if (more) pf.store(tiles[(w + 1) & 1]);
+      continue;
+    }
 
     // ---- front end: conv window, SiLU, softplus ----
     const int nvalid = (int)min<int64_t>(max<int64_t>(L - t0 - (int64_t)lane * K, 0), K);
@@ -388,6 +394,7 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
 #pragma unroll
       for (int j = 0; j < K; ++j) yv[j] *= silu(unpack<IO>(cz.w, j));
     }
+    if (more) pf.store(tiles[(w + 1) & 1]);
     store_lanes<IO, ALIGNED>(ry, voff, t0 * ES, yv);
   }
 
