@@ -161,6 +161,9 @@ def main():
     ap.add_argument("--chunk-hint", type=int, default=0, help="prefill decomposition (0 auto, 1 sequential, 8 windowed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--pool", action="store_true",
+                    help="serving form: ragged prompt lengths (uniform in [L/2, L]) and a cache pool of 2*batch "
+                         "entries addressed through a random slot map (ssm_prefill_pool / ssm_decode_step_pool)")
     ap.add_argument("--record-traffic", metavar="PMC_DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs and exit")
     args = ap.parse_args()
@@ -209,11 +212,27 @@ def main():
 
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    elems = B * L * D
+    if args.pool:
+        g = torch.Generator().manual_seed(1)
+        lens = torch.randint(L // 2, L + 1, (B,), generator=g, dtype=torch.int32)
+        lens[0] = L
+        pool = 2 * B
+        slots = torch.randperm(pool, generator=g)[:B].to(torch.int32)
+        elems = int(lens.sum()) * D
+        lens_d, slots_d = lens.to(dev), slots.to(dev)
+        hp = torch.zeros(pool, D, N, dtype=torch.float32, device=dev)
+        cp = torch.zeros(pool, D, CONV_W - 1, dtype=torch.float32, device=dev)
+        log(f"bench: pool form: {pool} cache entries, lengths {int(lens.min())}..{int(lens.max())}")
 
     def decode_loop(s=None):
         for t in range(T):
             tk = toks[t]
-            ssm.decode_step(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, h, c, y_t=ys[t], stream=s)
+            if args.pool:
+                ssm.decode_step_pool(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, slots_d, hp, cp,
+                                     y_t=ys[t], stream=s)
+            else:
+                ssm.decode_step(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, h, c, y_t=ys[t], stream=s)
 
     # The decode loop as a serving loop runs it: captured once in a HIP graph, replayed per
     # request.  (An eager, one-launch-per-call loop is timed separately below.)
@@ -233,8 +252,12 @@ def main():
     def step(marks):
         e0, e1, e2 = ev(), ev(), ev()
         e0.record(stream)
-        ssm.prefill(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], pd, y=y, h_out=h, conv_out=c,
-                    workspace=ws, stream=stream, chunk_hint=args.chunk_hint)
+        if args.pool:
+            ssm.prefill_pool(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], pd, slots_d, hp, cp,
+                             seqlens=lens_d, y=y, stream=stream, chunk_hint=args.chunk_hint)
+        else:
+            ssm.prefill(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], pd, y=y, h_out=h, conv_out=c,
+                        workspace=ws, stream=stream, chunk_hint=args.chunk_hint)
         e1.record(stream)
         if graph is not None:
             graph.replay()
@@ -268,9 +291,11 @@ def main():
     pre_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / len(marks)
     dec_ms = sum(b.elapsed_time(c_) for _, b, c_ in marks) / len(marks)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    elems = B * L * D
     gelem = elems / (pre_ms * 1e-3) / 1e9
     pbytes = prefill_bytes(B, L, D, N, es)
+    if args.pool:  # only the real tokens of each row move
+        ntok = elems // D
+        pbytes = ntok * D * 4 * es + ntok * 2 * N * es + B * D * (N + CONV_W - 1) * 4 + D * (N + 7) * 4
     dbytes = decode_bytes(B, D, N, es)
     p_gbps = pbytes / (pre_ms * 1e-3) / 1e9
     d_us = dec_ms * 1e3 / T if T else None
@@ -286,8 +311,10 @@ def main():
         "value": round(gelem, 3), "unit": "Gelem/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "seqlen": L, "d_inner": D, "d_state": N, "d_conv": CONV_W,
-                   "io": w.io, "state": "f32", "decode_steps": T, "parallelism": "none (one GPU's channel slice)"},
+        "config": {"workload": w.name + ("+pool" if args.pool else ""), "batch": B, "seqlen": L, "d_inner": D,
+                   "d_state": N, "d_conv": CONV_W, "io": w.io, "state": "f32", "decode_steps": T,
+                   "parallelism": "none (one GPU's channel slice)",
+                   "tokens": elems // D, "pool_entries": 2 * B if args.pool else None},
         "prefill_ms": round(pre_ms, 4),
         "decode_us_per_step": None if d_us is None else round(d_us, 3),
         "decode_mode": "hip_graph" if graph is not None else "eager",
@@ -300,6 +327,9 @@ def main():
                      "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
                      "flops_per_element": flops_per_element(N), "traffic": traffic},
     }
+    if args.pool and not args.no_cpu_baseline:
+        log("bench: the CPU baseline is defined on the full workload; skipped in the pool form")
+        args.no_cpu_baseline = True
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host cores")
         rec["cpu_baseline"] = cpu_baseline(w, prm, seq, toks)

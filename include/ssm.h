@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 #define SSM_MAX_STATE 16 /* largest supported d_state */
 #define SSM_CONV_WIDTH 4 /* the only supported d_conv */
 
@@ -151,6 +151,49 @@ int ssm_decode_step(const ssm_dims* dims, const ssm_params* params,
                     const void* x_t, const void* dt_t, const void* z_t,
                     const void* B_t, const void* C_t,
                     void* y_t, float* h, float* conv_state, void* stream);
+
+/*
+ * Serving forms: ragged batches and a cache pool.  A server keeps one h / conv entry per
+ * live request in a pool and runs whichever requests are ready, so batch row b maps to pool
+ * entry slots[b], and prefill rows may hold prompts of different lengths padded to L.
+ * Passages: state caching between prefill and decode (Methodology item 3 and the Key
+ * contributions list of the page cited above) with the batch sizes and context lengths the
+ * same page varies (Methodology item 5).
+ *
+ *   h_pool    [S, D, N] fp32 and conv_pool [S, D, 3] fp32, S = pool_size >= 1
+ *   slots     device int32 [B]: pool entry of batch row b; a value outside [0, S) skips row b
+ *             entirely (nothing of that row is read from or written to the pool, and its
+ *             outputs are left untouched).  Two rows naming the same entry race: undefined.
+ *   seqlens   device int32 [B] or NULL: row b runs its first clamp(seqlens[b], 0, L) tokens;
+ *             outputs past that length are left untouched.  NULL = L tokens for every row.
+ * The other tensors and all conventions are those of ssm_prefill / ssm_decode_step; the
+ * pools follow the prefill alignment rule in ssm_prefill_pool and h_pool 16-byte, conv_pool
+ * 4-byte, slots 4-byte in ssm_decode_step_pool.
+ */
+
+/*
+ * Prefill into a cache pool: for every row b with a valid slot, run its first n_b tokens and
+ * store the final state in h_pool[slots[b]], the last three raw inputs (before token n_b) in
+ * conv_pool[slots[b]].  resume != 0 starts each row from its pool entry (chunked prefill:
+ * prompts arrive in pieces); resume == 0 starts from the zero state and zero history.  The
+ * pool is read and rewritten in place.  The prefill decomposition is chosen as in
+ * ssm_prefill (dims->chunk_hint).
+ */
+int ssm_prefill_pool(const ssm_dims* dims, const ssm_params* params,
+                     const void* x, const void* dt, const void* z,
+                     const void* Bm, const void* Cm,
+                     const int32_t* seqlens, const int32_t* slots, int64_t pool_size, int resume,
+                     void* y, float* h_pool, float* conv_pool, void* stream);
+
+/*
+ * Decode step against a cache pool: row b reads and updates h_pool[slots[b]] and
+ * conv_pool[slots[b]] in place (rows with an invalid slot are skipped).
+ */
+int ssm_decode_step_pool(const ssm_dims* dims, const ssm_params* params,
+                         const void* x_t, const void* dt_t, const void* z_t,
+                         const void* B_t, const void* C_t,
+                         const int32_t* slots, int64_t pool_size,
+                         void* y_t, float* h_pool, float* conv_pool, void* stream);
 
 #ifdef __cplusplus
 }

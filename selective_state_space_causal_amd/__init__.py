@@ -5,4 +5,5 @@ HIP kernels for gfx950) through a thin ctypes binding; ``inputs`` makes seeded s
 workloads.  Importing the package does not load the library; the first call does, and
 raises if it is not built.
 """
-from ._lib import SsmError, decode_step, load, prefill, workspace_bytes  # noqa: F401
+from ._lib import (SsmError, decode_step, decode_step_pool, load, prefill, prefill_pool,  # noqa: F401
+                   workspace_bytes)

@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssm.so")
 
 SSM_F32, SSM_BF16 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_STATE = 16
 CONV_W = 4
 
@@ -61,6 +61,13 @@ def load(path: str = LIB_PATH):
     lib.ssm_prefill.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params)] + [vp] * 11 + [sz, vp]
     lib.ssm_decode_step.restype = ctypes.c_int
     lib.ssm_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params)] + [vp] * 9
+    i64, cint = ctypes.c_int64, ctypes.c_int
+    lib.ssm_prefill_pool.restype = ctypes.c_int
+    lib.ssm_prefill_pool.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params)] + [vp] * 7 + [i64, cint] + \
+        [vp] * 4
+    lib.ssm_decode_step_pool.restype = ctypes.c_int
+    lib.ssm_decode_step_pool.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params)] + [vp] * 6 + [i64] + \
+        [vp] * 4
     if lib.ssm_abi_version() != ABI_VERSION:
         raise ImportError(f"libssm ABI {lib.ssm_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -170,4 +177,68 @@ def decode_step(x_t, dt_t, z_t, B_t, C_t, params: dict, h, conv, *, y_t=None, st
                              _ptr(C_t), _ptr(y_t), _ptr(h), _ptr(conv), stream_handle(stream))
     if st != 0:
         raise SsmError("ssm_decode_step", st, lib.ssm_status_str(st).decode())
+    return y_t
+
+
+def _check_index(t, name, B, device, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != (B,) or t.dtype != torch.int32 or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor of shape ({B},) on {device}")
+
+
+def prefill_pool(x, dt, z, Bm, Cm, params: dict, slots, h_pool, conv_pool, *, seqlens=None, resume=False,
+                 chunk_hint: int = 0, y=None, stream=None):
+    """ssm_prefill_pool: rows write their final state into h_pool[slots[b]] / conv_pool[slots[b]]
+    (resume=True starts from those entries); seqlens [B] int32 gives per-row lengths.  Returns y."""
+    lib = load()
+    Bsz, D, L = x.shape
+    N = params["A"].shape[1]
+    dev, io = x.device, x.dtype
+    for t, n in ((x, "x"), (dt, "dt"), (z, "z")):
+        _check(t, n, (Bsz, D, L), io, dev, optional=(n == "z"))
+    _check(Bm, "Bm", (Bsz, L, N), io, dev)
+    _check(Cm, "Cm", (Bsz, L, N), io, dev)
+    _check_index(slots, "slots", Bsz, dev)
+    _check_index(seqlens, "seqlens", Bsz, dev, optional=True)
+    S = h_pool.shape[0]
+    _check(h_pool, "h_pool", (S, D, N), torch.float32, dev)
+    _check(conv_pool, "conv_pool", (S, D, CONV_W - 1), torch.float32, dev)
+    _check_params(params, D, N, dev)
+    y = torch.empty_like(x) if y is None else y
+    d = Dims(Bsz, L, D, N, CONV_W, _io_code(io), chunk_hint)
+    p = make_params(params)
+    st = lib.ssm_prefill_pool(ctypes.byref(d), ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(z), _ptr(Bm), _ptr(Cm),
+                              _ptr(seqlens), _ptr(slots), S, int(bool(resume)), _ptr(y), _ptr(h_pool),
+                              _ptr(conv_pool), stream_handle(stream))
+    if st != 0:
+        raise SsmError("ssm_prefill_pool", st, lib.ssm_status_str(st).decode())
+    return y
+
+
+def decode_step_pool(x_t, dt_t, z_t, B_t, C_t, params: dict, slots, h_pool, conv_pool, *, y_t=None, stream=None):
+    """ssm_decode_step_pool: row b updates h_pool[slots[b]] / conv_pool[slots[b]] in place.  Returns y_t."""
+    lib = load()
+    Bsz, D = x_t.shape
+    N = params["A"].shape[1]
+    dev, io = x_t.device, x_t.dtype
+    for t, n in ((x_t, "x_t"), (dt_t, "dt_t"), (z_t, "z_t")):
+        _check(t, n, (Bsz, D), io, dev, optional=(n == "z_t"))
+    _check(B_t, "B_t", (Bsz, N), io, dev)
+    _check(C_t, "C_t", (Bsz, N), io, dev)
+    _check_index(slots, "slots", Bsz, dev)
+    S = h_pool.shape[0]
+    _check(h_pool, "h_pool", (S, D, N), torch.float32, dev)
+    _check(conv_pool, "conv_pool", (S, D, CONV_W - 1), torch.float32, dev)
+    _check_params(params, D, N, dev)
+    y_t = torch.empty_like(x_t) if y_t is None else y_t
+    d = Dims(Bsz, 1, D, N, CONV_W, _io_code(io), 0)
+    p = make_params(params)
+    st = lib.ssm_decode_step_pool(ctypes.byref(d), ctypes.byref(p), _ptr(x_t), _ptr(dt_t), _ptr(z_t), _ptr(B_t),
+                                  _ptr(C_t), _ptr(slots), S, _ptr(y_t), _ptr(h_pool), _ptr(conv_pool),
+                                  stream_handle(stream))
+    if st != 0:
+        raise SsmError("ssm_decode_step_pool", st, lib.ssm_status_str(st).decode())
     return y_t

@@ -78,6 +78,27 @@ ssm::ScanArgs make_args(const ssm_dims* d, const ssm_params* p) {
   return a;
 }
 
+// Every output range must miss every input range and every other output range.
+int check_overlaps(const void* const* ins, const int64_t* in_bytes, int nins, const void* const* outs,
+                   const int64_t* out_bytes, int nouts) {
+  for (int o = 0; o < nouts; ++o) {
+    for (int i = 0; i < nins; ++i)
+      if (overlaps(span(outs[o], out_bytes[o]), span(ins[i], in_bytes[i]))) return SSM_ERR_ALIAS;
+    for (int q = o + 1; q < nouts; ++q)
+      if (overlaps(span(outs[o], out_bytes[o]), span(outs[q], out_bytes[q]))) return SSM_ERR_ALIAS;
+  }
+  return SSM_OK;
+}
+
+// Cache-pool sizes: S * D * N and S * D * 3 fp32 values must not overflow.
+int check_pool(const ssm_dims* d, int64_t pool) {
+  int64_t bytes;
+  if (pool < 1 || !tensor_bytes(pool, d->d_inner, d->d_state, 4, &bytes) ||
+      !tensor_bytes(pool, d->d_inner, 3, 4, &bytes))
+    return SSM_ERR_SHAPE;
+  return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +216,93 @@ int ssm_decode_step(const ssm_dims* d, const ssm_params* p, const void* x_t, con
   a.y = y_t;
   a.h_out = h;
   a.conv_out = conv_state;
+  (void)hipGetLastError();
+  if (ssm::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return SSM_ERR_LAUNCH;
+  return SSM_OK;
+}
+
+int ssm_prefill_pool(const ssm_dims* d, const ssm_params* p, const void* x, const void* dt, const void* z,
+                     const void* Bm, const void* Cm, const int32_t* seqlens, const int32_t* slots,
+                     int64_t pool_size, int resume, void* y, float* h_pool, float* conv_pool, void* stream) {
+  int st = check_dims(d, true);
+  if (st != SSM_OK) return st;
+  if (!x || !dt || !Bm || !Cm || !slots || !y || !h_pool || !conv_pool) return SSM_ERR_NULL;
+  st = check_pool(d, pool_size);
+  if (st != SSM_OK) return st;
+  const int64_t B = d->batch, L = d->seqlen, D = d->d_inner, N = d->d_state, S = pool_size;
+  const int64_t es = d->io_dtype == SSM_BF16 ? 2 : 4;
+  const int64_t seq = B * D * L * es, bc = B * L * N * es, hb = S * D * N * 4, cvb = S * D * 3 * 4;
+  const void* ins[7] = {x, dt, z, Bm, Cm, seqlens, slots};
+  const int64_t in_bytes[7] = {seq, seq, seq, bc, bc, B * 4, B * 4};
+  const void* outs[3] = {y, h_pool, conv_pool};
+  const int64_t out_bytes[3] = {seq, hb, cvb};
+  for (int i = 0; i < 5; ++i)
+    if (ins[i] && !aligned16(ins[i])) return SSM_ERR_ALIGN;
+  if ((seqlens && !aligned(seqlens, 4)) || !aligned(slots, 4)) return SSM_ERR_ALIGN;
+  for (int o = 0; o < 3; ++o)
+    if (!aligned16(outs[o])) return SSM_ERR_ALIGN;
+  st = check_params(p, outs, out_bytes, 3, D, N);
+  if (st != SSM_OK) return st;
+  st = check_overlaps(ins, in_bytes, 7, outs, out_bytes, 3);
+  if (st != SSM_OK) return st;
+
+  ssm::ScanArgs a = make_args(d, p);
+  a.x = x;
+  a.dt = dt;
+  a.z = z;
+  a.Bm = Bm;
+  a.Cm = Cm;
+  a.h0 = resume ? h_pool : nullptr;  // each cache entry is read before it is rewritten, by the same wave
+  a.conv0 = resume ? conv_pool : nullptr;
+  a.y = y;
+  a.h_out = h_pool;
+  a.conv_out = conv_pool;
+  a.seqlens = seqlens;
+  a.slots = slots;
+  a.pool = S;
+  if (ssm::prefill_workspace_bytes(a) != 0) return SSM_ERR_WORKSPACE;  // no variant here needs scratch
+  (void)hipGetLastError();
+  if (ssm::launch_prefill(a, nullptr, static_cast<hipStream_t>(stream)) != hipSuccess) return SSM_ERR_LAUNCH;
+  return SSM_OK;
+}
+
+int ssm_decode_step_pool(const ssm_dims* d, const ssm_params* p, const void* x_t, const void* dt_t,
+                         const void* z_t, const void* B_t, const void* C_t, const int32_t* slots,
+                         int64_t pool_size, void* y_t, float* h_pool, float* conv_pool, void* stream) {
+  int st = check_dims(d, false);
+  if (st != SSM_OK) return st;
+  if (!x_t || !dt_t || !B_t || !C_t || !slots || !y_t || !h_pool || !conv_pool) return SSM_ERR_NULL;
+  st = check_pool(d, pool_size);
+  if (st != SSM_OK) return st;
+  const int64_t B = d->batch, D = d->d_inner, N = d->d_state, S = pool_size;
+  const int64_t es = d->io_dtype == SSM_BF16 ? 2 : 4;
+  const int64_t tok = B * D * es, bc = B * N * es, hb = S * D * N * 4, cvb = S * D * 3 * 4;
+  const void* ins[6] = {x_t, dt_t, z_t, B_t, C_t, slots};
+  const int64_t in_bytes[6] = {tok, tok, tok, bc, bc, B * 4};
+  const void* outs[3] = {y_t, h_pool, conv_pool};
+  const int64_t out_bytes[3] = {tok, hb, cvb};
+  for (int i = 0; i < 5; ++i)
+    if (ins[i] && !aligned(ins[i], (uintptr_t)es)) return SSM_ERR_ALIGN;
+  if (!aligned(slots, 4) || !aligned(y_t, (uintptr_t)es) || !aligned16(h_pool) || !aligned(conv_pool, 4))
+    return SSM_ERR_ALIGN;
+  st = check_params(p, outs, out_bytes, 3, D, N);
+  if (st != SSM_OK) return st;
+  st = check_overlaps(ins, in_bytes, 6, outs, out_bytes, 3);
+  if (st != SSM_OK) return st;
+  ssm::ScanArgs a = make_args(d, p);
+  a.L = 1;
+  a.x = x_t;
+  a.dt = dt_t;
+  a.z = z_t;
+  a.Bm = B_t;
+  a.Cm = C_t;
+  a.h0 = h_pool;
+  a.conv0 = conv_pool;
+  a.y = y_t;
+  a.h_out = h_pool;
+  a.conv_out = conv_pool;
+  a.slots = slots;
+  a.pool = S;
   (void)hipGetLastError();
   if (ssm::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess) return SSM_ERR_LAUNCH;
   return SSM_OK;

@@ -29,16 +29,18 @@ __global__ __launch_bounds__(256) void decode_quad(ScanArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t rows = a.B * a.D;
   const int64_t row = min(gid >> 2, rows - 1);  // a ragged tail repeats the last channel, writes nothing
-  const bool live = (gid >> 2) < rows;
   const int q = (int)(gid & 3);
   const int64_t b = row / a.D, c = row - b * a.D;
+  int64_t crow;  // cache (h / conv) row; a skipped batch row leaves as a whole quad (no DPP partner lost)
+  if (!cache_row(a, b, c, crow)) return;
+  const bool live = (gid >> 2) < rows;
 
   const float4 w = *reinterpret_cast<const float4*>(a.conv_w + c * 4);
   const float cb = a.conv_b ? a.conv_b[c] : 0.0f;
   const float dtb = a.dt_bias[c], dsk = a.Dskip[c];
   const float4 A4 = *reinterpret_cast<const float4*>(a.A + c * 16 + q * QS);
-  const float4 h4 = *reinterpret_cast<const float4*>(a.h0 + row * 16 + q * QS);
-  const float* cv = a.conv0 + row * 3;
+  const float4 h4 = *reinterpret_cast<const float4*>(a.h0 + crow * 16 + q * QS);
+  const float* cv = a.conv0 + crow * 3;
   const float x0 = cv[0], x1 = cv[1], x2 = cv[2];
   const IO* Bt = static_cast<const IO*>(a.Bm) + b * 16 + q * QS;
   const IO* Ct = static_cast<const IO*>(a.Cm) + b * 16 + q * QS;
@@ -62,10 +64,10 @@ __global__ __launch_bounds__(256) void decode_quad(ScanArgs a) {
   r = fmaf(dsk, u, r);
   if (a.z) r *= silu(to_f32(static_cast<const IO*>(a.z)[row]));
   if (!live) return;
-  *reinterpret_cast<float4*>(a.h_out + row * 16 + q * QS) = make_float4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<float4*>(a.h_out + crow * 16 + q * QS) = make_float4(h[0], h[1], h[2], h[3]);
   if (q == 0) {
     static_cast<IO*>(a.y)[row] = from_f32<IO>(r);
-    float* co = a.conv_out + row * 3;
+    float* co = a.conv_out + crow * 3;
     co[0] = x1;
     co[1] = x2;
     co[2] = xt;

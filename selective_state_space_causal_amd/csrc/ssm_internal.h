@@ -29,7 +29,30 @@ struct ScanArgs {
   int N;
   int bf16;        // io dtype: 1 = bf16, 0 = fp32
   int chunk_hint;  // prefill decomposition override (0 = automatic)
+  // Serving form (cache pool): nullable.
+  const int32_t* seqlens;  // [B] tokens of each batch row to run (clamped to [0, L]); null: all L
+  const int32_t* slots;    // [B] cache-pool entry of each batch row; outside [0, pool) skips the row
+  int64_t pool;            // entries of the cache pool when slots is set
 };
+
+// Cache row (h / conv entry) of channel c of batch row b, or false when the row is skipped.
+__device__ __forceinline__ bool cache_row(const ScanArgs& a, int64_t b, int64_t c, int64_t& crow) {
+  if (!a.slots) {
+    crow = b * a.D + c;
+    return true;
+  }
+  const int64_t s = a.slots[b];
+  if (s < 0 || s >= a.pool) return false;
+  crow = s * a.D + c;
+  return true;
+}
+
+// Tokens to run for batch row b.
+__device__ __forceinline__ int64_t row_len(const ScanArgs& a, int64_t b) {
+  if (!a.seqlens) return a.L;
+  const int64_t n = a.seqlens[b];
+  return n < 0 ? 0 : (n > a.L ? a.L : n);
+}
 
 // Prefill decompositions.
 // chunk_hint selects one explicitly; 0 lets choose_prefill_variant decide.

@@ -64,17 +64,20 @@ __global__ __launch_bounds__(256) void prefill_sequential(ScanArgs a) {
   if (row >= a.B * a.D) return;
   const int64_t b = row / a.D, c = row - b * a.D;
   const int N = EXACT ? NMAX : a.N;
-  const int64_t L = a.L;
+  const int64_t L = a.L;            // row stride
+  int64_t crow;                     // cache (h / conv) row
+  if (!cache_row(a, b, c, crow)) return;
+  const int64_t Lb = row_len(a, b);  // tokens to run
   Channel<NMAX> ch;
   load_channel<NMAX, EXACT>(a, c, ch);
   float h[NMAX];
 #pragma unroll
-  for (int n = 0; n < NMAX; ++n) h[n] = (a.h0 && (EXACT || n < N)) ? a.h0[row * N + n] : 0.0f;
+  for (int n = 0; n < NMAX; ++n) h[n] = (a.h0 && (EXACT || n < N)) ? a.h0[crow * N + n] : 0.0f;
   float hist[3] = {0.0f, 0.0f, 0.0f};
   if (a.conv0) {
-    hist[0] = a.conv0[row * 3 + 0];
-    hist[1] = a.conv0[row * 3 + 1];
-    hist[2] = a.conv0[row * 3 + 2];
+    hist[0] = a.conv0[crow * 3 + 0];
+    hist[1] = a.conv0[crow * 3 + 1];
+    hist[2] = a.conv0[crow * 3 + 2];
   }
   const IO* x = static_cast<const IO*>(a.x) + row * L;
   const IO* dt = static_cast<const IO*>(a.dt) + row * L;
@@ -82,17 +85,17 @@ __global__ __launch_bounds__(256) void prefill_sequential(ScanArgs a) {
   const IO* Bm = static_cast<const IO*>(a.Bm) + b * L * N;
   const IO* Cm = static_cast<const IO*>(a.Cm) + b * L * N;
   IO* y = static_cast<IO*>(a.y) + row * L;
-  for (int64_t t = 0; t < L; ++t) {
+  for (int64_t t = 0; t < Lb; ++t) {
     const float r = token<IO, NMAX, EXACT>(ch, N, h, hist, to_f32(x[t]), to_f32(dt[t]), Bm + t * N, Cm + t * N,
                                            z ? z + t : nullptr);
     y[t] = from_f32<IO>(r);
   }
 #pragma unroll
   for (int n = 0; n < NMAX; ++n)
-    if (EXACT || n < N) a.h_out[row * N + n] = h[n];
-  a.conv_out[row * 3 + 0] = hist[0];
-  a.conv_out[row * 3 + 1] = hist[1];
-  a.conv_out[row * 3 + 2] = hist[2];
+    if (EXACT || n < N) a.h_out[crow * N + n] = h[n];
+  a.conv_out[crow * 3 + 0] = hist[0];
+  a.conv_out[crow * 3 + 1] = hist[1];
+  a.conv_out[crow * 3 + 2] = hist[2];
 }
 
 // Decode step: each lane reads its channel's cache, runs one token and writes the cache back
@@ -103,12 +106,14 @@ __global__ __launch_bounds__(256) void decode_step(ScanArgs a) {
   if (row >= a.B * a.D) return;
   const int64_t b = row / a.D, c = row - b * a.D;
   const int N = EXACT ? NMAX : a.N;
+  int64_t crow;  // cache (h / conv) row
+  if (!cache_row(a, b, c, crow)) return;
   Channel<NMAX> ch;
   load_channel<NMAX, EXACT>(a, c, ch);
   float h[NMAX];
 #pragma unroll
-  for (int n = 0; n < NMAX; ++n) h[n] = (EXACT || n < N) ? a.h0[row * N + n] : 0.0f;
-  float hist[3] = {a.conv0[row * 3 + 0], a.conv0[row * 3 + 1], a.conv0[row * 3 + 2]};
+  for (int n = 0; n < NMAX; ++n) h[n] = (EXACT || n < N) ? a.h0[crow * N + n] : 0.0f;
+  float hist[3] = {a.conv0[crow * 3 + 0], a.conv0[crow * 3 + 1], a.conv0[crow * 3 + 2]};
   const IO* zt = a.z ? static_cast<const IO*>(a.z) + row : nullptr;
   const float r = token<IO, NMAX, EXACT>(ch, N, h, hist, to_f32(static_cast<const IO*>(a.x)[row]),
                                          to_f32(static_cast<const IO*>(a.dt)[row]),
@@ -117,10 +122,10 @@ __global__ __launch_bounds__(256) void decode_step(ScanArgs a) {
   static_cast<IO*>(a.y)[row] = from_f32<IO>(r);
 #pragma unroll
   for (int n = 0; n < NMAX; ++n)
-    if (EXACT || n < N) a.h_out[row * N + n] = h[n];
-  a.conv_out[row * 3 + 0] = hist[0];
-  a.conv_out[row * 3 + 1] = hist[1];
-  a.conv_out[row * 3 + 2] = hist[2];
+    if (EXACT || n < N) a.h_out[crow * N + n] = h[n];
+  a.conv_out[crow * 3 + 0] = hist[0];
+  a.conv_out[crow * 3 + 1] = hist[1];
+  a.conv_out[crow * 3 + 2] = hist[2];
 }
 
 static inline dim3 rows_grid(const ScanArgs& a) {

@@ -171,8 +171,25 @@ struct Lanes {
   }
 };
 
+// Store the lane's first `nvalid` outputs (all K as vector stores when the lane is whole).
 template <typename IO, bool ALIGNED>
-__device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&v)[K]) {
+__device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&v)[K],
+                                            int nvalid) {
+  if (nvalid < K) {
+    if (nvalid > 0) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        if (j < nvalid) {
+          if constexpr (sizeof(IO) == 2)
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(v[j], 0.0f) & 0xFFFFu), r,
+                                                  voff + 2 * j, soff, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), r, voff + 4 * j, soff, 0);
+        }
+      }
+    }
+    return;
+  }
   if constexpr (sizeof(IO) == 2) {
     uint32_t w[K / 2];
 #pragma unroll
@@ -261,10 +278,13 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
   const int64_t b = blockIdx.x / groups;
   const int64_t c = (blockIdx.x - b * groups) * W + wave;
   const bool active = c < a.D;  // a ragged last group: idle waves still stage tiles and meet barriers
-  const int64_t L = a.L;
+  const int64_t L = a.L;                 // row stride of x, dt, z, y and B / C
   const int64_t cc = active ? c : 0;
   const int64_t row = b * a.D + cc;
   const int64_t row_bytes = L * ES;
+  int64_t crow;                          // cache (h / conv) row
+  if (!cache_row(a, b, cc, crow)) return;  // a skipped batch row: the whole workgroup leaves together
+  const int64_t Lb = row_len(a, b);      // tokens to run for this batch row
 
   const auto rx = row_rsrc(static_cast<const IO*>(a.x) + row * L, row_bytes);
   const auto rdt = row_rsrc(static_cast<const IO*>(a.dt) + row * L, row_bytes);
@@ -283,17 +303,17 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
 #pragma unroll
   for (int n = 0; n < NS; ++n) {
     A2[n] = a.A[cc * NS + n] * kLog2e;
-    carry[n] = a.h0 ? a.h0[row * NS + n] : 0.0f;
+    carry[n] = a.h0 ? a.h0[crow * NS + n] : 0.0f;
   }
   float hist0 = 0.0f, hist1 = 0.0f, hist2 = 0.0f;  // raw x[t0-3], x[t0-2], x[t0-1]
   if (a.conv0) {
-    hist0 = a.conv0[row * 3 + 0];
-    hist1 = a.conv0[row * 3 + 1];
-    hist2 = a.conv0[row * 3 + 2];
+    hist0 = a.conv0[crow * 3 + 0];
+    hist1 = a.conv0[crow * 3 + 1];
+    hist2 = a.conv0[crow * 3 + 2];
   }
   const float init0 = hist0, init1 = hist1, init2 = hist2;
 
-  const int nwin = (int)((L + WIN - 1) / WIN);
+  const int nwin = (int)((Lb + WIN - 1) / WIN);
   const int voff = lane * K * ES;  // this lane's byte offset inside a window
   TileChunks<IO> pf;
   Lanes<IO, ALIGNED> px, pdt, pz;
@@ -323,7 +343,7 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
     }
 
     // ---- front end: conv window, SiLU, softplus ----
-    const int nvalid = (int)min<int64_t>(max<int64_t>(L - t0 - (int64_t)lane * K, 0), K);
+    const int nvalid = (int)min<int64_t>(max<int64_t>(Lb - t0 - (int64_t)lane * K, 0), K);
     float xv[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) xv[j] = unpack<IO>(cx.w, j);
@@ -395,18 +415,18 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
       for (int j = 0; j < K; ++j) yv[j] *= silu(unpack<IO>(cz.w, j));
     }
     if (more) pf.store(tiles[(w + 1) & 1]);
-    store_lanes<IO, ALIGNED>(ry, voff, t0 * ES, yv);
+    store_lanes<IO, ALIGNED>(ry, voff, t0 * ES, yv, nvalid);
   }
 
   if (active && lane == 0) {
 #pragma unroll
-    for (int n = 0; n < NS; ++n) a.h_out[row * NS + n] = carry[n];
+    for (int n = 0; n < NS; ++n) a.h_out[crow * NS + n] = carry[n];
     const float init[3] = {init0, init1, init2};
     const IO* xr = static_cast<const IO*>(a.x) + row * L;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      const int64_t t = L - 3 + j;  // raw input xi[L-3+j]; history below zero
-      a.conv_out[row * 3 + j] = t >= 0 ? to_f32(xr[t]) : init[t + 3];
+      const int64_t t = Lb - 3 + j;  // raw input xi[Lb-3+j]; history below zero
+      a.conv_out[crow * 3 + j] = t >= 0 ? to_f32(xr[t]) : init[t + 3];
     }
   }
 }

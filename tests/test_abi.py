@@ -155,3 +155,39 @@ def test_binding_fails_loudly_without_library(tmp_path):
             L.load(str(tmp_path / "missing.so"))
     finally:
         L._lib = saved
+
+
+def prefill_pool(d, p, **over):
+    a = dict(x=fake(0), dt=fake(1), z=fake(2), Bm=fake(3), Cm=fake(4), seqlens=fake(8), slots=fake(9), pool=6,
+             resume=0, y=fake(5), h=fake(6), conv=fake(7))
+    a.update(over)
+    return L.load().ssm_prefill_pool(None if d is None else ctypes.byref(d), None if p is None else ctypes.byref(p),
+                                     a["x"], a["dt"], a["z"], a["Bm"], a["Cm"], a["seqlens"], a["slots"], a["pool"],
+                                     a["resume"], a["y"], a["h"], a["conv"], None)
+
+
+def decode_pool(d, p, **over):
+    a = dict(x=fake(0), dt=fake(1), z=fake(2), Bt=fake(3), Ct=fake(4), slots=fake(9), pool=6, y=fake(5), h=fake(6),
+             conv=fake(7))
+    a.update(over)
+    return L.load().ssm_decode_step_pool(None if d is None else ctypes.byref(d), None if p is None else ctypes.byref(p),
+                                         a["x"], a["dt"], a["z"], a["Bt"], a["Ct"], a["slots"], a["pool"], a["y"],
+                                         a["h"], a["conv"], None)
+
+
+def test_pool_entry_points_validation():
+    for fn in (prefill_pool, decode_pool):
+        assert fn(None, params()) == NULL
+        assert fn(dims(), params(), slots=None) == NULL
+        assert fn(dims(), params(), h=None) == NULL
+        assert fn(dims(), params(), pool=0) == SHAPE
+        assert fn(dims(), params(), pool=1 << 60) == SHAPE   # S * D * N * 4 bytes overflow
+        assert fn(dims(d_state=0), params()) == SHAPE
+        assert fn(dims(), params(), slots=fake(9, 2)) == ALIGN
+        assert fn(dims(), params(), h=fake(6, 4)) == ALIGN
+        assert fn(dims(), params(), h=fake(0)) == ALIAS            # pool over x
+        assert fn(dims(), params(), slots=fake(5)) == ALIAS        # y over slots
+        assert fn(dims(), params(), conv=fake(6, 64)) == ALIAS     # conv pool inside the h pool
+    assert prefill_pool(dims(), params(), seqlens=fake(8, 2)) == ALIGN
+    assert prefill_pool(dims(), params(), seqlens=fake(5, 0)) == ALIAS   # y over seqlens
+    assert prefill_pool(dims(chunk_hint=5), params()) == SHAPE
