@@ -273,7 +273,9 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
   __shared__ Tile tiles[2];  // window w reads tiles[w & 1] while window w + 1's goes into the other
   constexpr int ES = sizeof(IO);
   const int lane = threadIdx.x & (WAVE - 1);
-  const int wave = threadIdx.x / WAVE;
+  // Wave-uniform by construction; saying so keeps the row descriptors below in SGPRs (a
+  // descriptor the compiler cannot prove uniform costs a readfirstlane loop per access).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int64_t groups = (a.D + W - 1) / W;
   const int64_t b = blockIdx.x / groups;
   const int64_t c = (blockIdx.x - b * groups) * W + wave;
@@ -343,7 +345,9 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
     }
 
     // ---- front end: conv window, SiLU, softplus ----
-    const int nvalid = (int)min<int64_t>(max<int64_t>(Lb - t0 - (int64_t)lane * K, 0), K);
+    const int64_t left = Lb - t0;  // >= 1, uniform
+    const int rem = left < WIN ? (int)left : WIN;
+    const int nvalid = rem - lane * K < 0 ? 0 : (rem - lane * K > K ? K : rem - lane * K);
     float xv[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) xv[j] = unpack<IO>(cx.w, j);
@@ -363,7 +367,9 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
       const float s1 = j >= 1 ? xv[j - 1] : xm1;
       const float v = fmaf(w3, xv[j], fmaf(w2, s1, fmaf(w1, s2, fmaf(w0, s3, cb))));
       const float u = silu(v);
-      const float d = j < nvalid ? softplus(unpack<IO>(cdt.w, j) + dtb) : 0.0f;  // 0: identity step
+      // Past the row end the step is an identity: softplus(-inf) is exactly 0.  Selecting the
+      // argument (not the result) keeps this branch-free.
+      const float d = softplus(j < nvalid ? unpack<IO>(cdt.w, j) + dtb : -__builtin_inff());
       dl[j] = d;
       du[j] = d * u;
       yv[j] = dsk * u;
