@@ -8,9 +8,9 @@
 //   1. lane i takes tokens [t0 + i*K, t0 + (i+1)*K): loads x / dt / z with one 16-byte
 //      vector load each, runs the conv + SiLU + softplus front end in registers (the
 //      three previous raw inputs come from lane i-1 through a DPP wave shift);
-//   2. per group of 4 states, each lane reduces its K tokens to one affine pair
-//      (P, H) = (prod a_t, state reached from zero), keeping every a_t and b_t in
-//      registers;
+//   2. per group of states (8 for bf16 io, 4 for fp32 io), each lane reduces its K tokens
+//      to one affine pair (P, H) = (prod a_t, state reached from zero), keeping every a_t
+//      and b_t in registers;
 //   3. a Kogge-Stone scan of the pairs across the 64 lanes with DPP (row_shr 1/2/4/8,
 //      row_bcast 15/31) gives each lane the state entering its tokens, seeded with the
 //      carry of the previous window; lane 63's total becomes the next carry;
@@ -32,7 +32,12 @@ constexpr int WAVE = 64;
 constexpr int WIN = WAVE * K;       // tokens per window
 constexpr int W = 8;                // waves (channels) per workgroup
 constexpr int THREADS = W * WAVE;
-constexpr int G = 4;                // states per replay group
+// States per replay group: 8 independent chains per pass for bf16 io (more in flight per wave;
+// fits the 256-VGPR budget of two waves per SIMD), 4 for fp32 io, whose wider prefetch
+// registers would otherwise spill.  Per state the arithmetic is the same either way, so the
+// two choices give bit-identical results.
+template <typename IO>
+constexpr int group_states() { return sizeof(IO) == 2 ? 8 : 4; }
 constexpr int LANE_STRIDE = K * NS + 4;  // floats per lane block in LDS (+4: conflict-free b128)
 
 // GFX9 DPP control: each lane reads lane - 1 of the whole wave (lane 0 has no source).
@@ -379,6 +384,7 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
     // ---- state groups: local pairs, lane scan, replay ----
     const float* tb = &tile.B[lane * LANE_STRIDE];
     const float* tcp = &tile.C[lane * LANE_STRIDE];
+    constexpr int G = group_states<IO>();
 #pragma unroll
     for (int q0 = 0; q0 < NS; q0 += G) {
       float av[K][G], bv[K][G], P[G], H[G];
@@ -389,8 +395,15 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        const float4 Bq = *reinterpret_cast<const float4*>(tb + j * NS + q0);
-        const float bq[4] = {Bq.x, Bq.y, Bq.z, Bq.w};
+        float bq[G];
+#pragma unroll
+        for (int g = 0; g < G; g += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(tb + j * NS + q0 + g);
+          bq[g] = v.x;
+          bq[g + 1] = v.y;
+          bq[g + 2] = v.z;
+          bq[g + 3] = v.w;
+        }
 #pragma unroll
         for (int q = 0; q < G; ++q) {
           av[j][q] = hw_exp2(dl[j] * A2[q0 + q]);
@@ -401,13 +414,22 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
       float hc[G], cg[G];
 #pragma unroll
       for (int q = 0; q < G; ++q) cg[q] = carry[q0 + q];
-      scan4(P, H, cg, hc);
+#pragma unroll
+      for (int g = 0; g < G; g += 4) scan4(*reinterpret_cast<float(*)[4]>(&P[g]), *reinterpret_cast<float(*)[4]>(&H[g]),
+                                           *reinterpret_cast<float(*)[4]>(&cg[g]), *reinterpret_cast<float(*)[4]>(&hc[g]));
 #pragma unroll
       for (int q = 0; q < G; ++q) carry[q0 + q] = cg[q];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        const float4 Cq = *reinterpret_cast<const float4*>(tcp + j * NS + q0);
-        const float cq[4] = {Cq.x, Cq.y, Cq.z, Cq.w};
+        float cq[G];
+#pragma unroll
+        for (int g = 0; g < G; g += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(tcp + j * NS + q0 + g);
+          cq[g] = v.x;
+          cq[g + 1] = v.y;
+          cq[g + 2] = v.z;
+          cq[g + 3] = v.w;
+        }
 #pragma unroll
         for (int q = 0; q < G; ++q) {
           hc[q] = fmaf(av[j][q], hc[q], bv[j][q]);
