@@ -57,9 +57,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload):
-    """HBM traffic per prefill launch from the committed rocprofv3 --pmc summary, or None when
-    there is none for this workload or the kernels changed since it was taken."""
+def traffic_from_profiles(workload, kernel=None):
+    """HBM traffic per launch (of the prefill kernel, or of `kernel`'s entry) from the committed
+    rocprofv3 --pmc summary, or None when there is none for this workload or the kernels
+    changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -69,12 +70,17 @@ def traffic_from_profiles(workload):
         return None
     if not rec or rec.get("source_hash") != kernel_source_hash():
         return None
+    if kernel is not None:
+        return (rec.get(kernel) or {}).get("bytes_per_launch")
     return rec.get("bytes_per_launch")
 
 
 PMC_COMMAND = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} -d $REPO/gpurun_out/pmc -o {ctr} "
                "--output-format csv -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline "
                "--decode-steps 8 --copy-calibration --workload {workload}")
+PMC_COMMAND_CODEC = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} -d $REPO/gpurun_out/pmc_codec -o {ctr} "
+                     "--output-format csv -- python3 $REPO/bench.py --codec {workload} --steps 2 --warmup 1 "
+                     "--no-cpu-baseline --copy-calibration")
 
 
 def record_traffic(pmc_dir, workload):
@@ -111,12 +117,17 @@ def record_traffic(pmc_dir, workload):
 
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
-    entry = {"source_hash": kernel_source_hash(), "command": PMC_COMMAND.format(ctr="<FETCH_SIZE|WRITE_SIZE>",
-                                                                                 workload=workload),
+    codec = kernel("q8_") is not None
+    cmd = (PMC_COMMAND_CODEC if codec else PMC_COMMAND).format(ctr="<FETCH_SIZE|WRITE_SIZE>", workload=workload)
+    entry = {"source_hash": kernel_source_hash(), "command": cmd,
              "copy_calibration": {"kernel": copy_name, "fetch_scale": round(fetch_scale, 4),
-                                  "write_scale": round(write_scale, 4)},
-             "prefill": kernel("prefill_"), "decode": kernel("decode_")}
-    entry["bytes_per_launch"] = entry["prefill"]["bytes_per_launch"] if entry["prefill"] else None
+                                  "write_scale": round(write_scale, 4)}}
+    if codec:
+        entry.update({"quantize": kernel("q8_quantize"), "dequant_sum": kernel("q8_dequant_sum")})
+        entry["bytes_per_launch"] = entry["quantize"]["bytes_per_launch"] if entry["quantize"] else None
+    else:
+        entry.update({"prefill": kernel("prefill_"), "decode": kernel("decode_")})
+        entry["bytes_per_launch"] = entry["prefill"]["bytes_per_launch"] if entry["prefill"] else None
     rec[workload] = entry
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -148,6 +159,115 @@ def cpu_baseline(w, prm, seq_dev, toks_dev):
             "prefill_s": round(t1 - t0, 3), "decode_us_per_step": round((t3 - t2) / max(T, 1) * 1e6, 1)}
 
 
+def codec_bytes(n, nb, es, parts):
+    """Algorithmic HBM bytes of the codec kernels: quantize reads the io tensor and writes one
+    code per element plus one fp32 scale per block; dequant-sum reads every part's codes and
+    scales and writes the io tensor."""
+    return n * es + n + 4 * nb, parts * (n + 4 * nb) + n * es
+
+
+def codec_cpu_baseline(xs_dev, block, elems_sample):
+    """Time the numpy codec oracle on the host on a bounded sample: the first `elems_sample`
+    elements of every part, quantized, then dequantized and summed."""
+    import numpy as np
+    from oracle import codec as C
+
+    xs = [x[:elems_sample].float().cpu().numpy() for x in xs_dev]
+    t0 = time.perf_counter()
+    enc = [C.quantize(x, block) for x in xs]
+    t1 = time.perf_counter()
+    C.dequantize_sum(np.stack([e[0] for e in enc]), np.stack([e[1] for e in enc]), block)
+    t2 = time.perf_counter()
+    n, nb, P = elems_sample, -(-elems_sample // block), len(xs)
+    qb, db = codec_bytes(n, nb, 2, P)
+    t_step = (t1 - t0) / P + (t2 - t1)
+    return {"value": round((qb + db) / t_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {elems_sample} elements of each of the {P} parts: quantize (time per part) plus the "
+                      f"{P}-part dequant-sum, numpy on one thread; algorithmic bytes of that sample / time",
+            "quantize_s_per_part": round((t1 - t0) / P, 4), "dequant_sum_s": round(t2 - t1, 4)}
+
+
+def bench_codec(args):
+    """One step = quantize this rank's partial + dequantize-and-sum the P parts received."""
+    import torch
+
+    import selective_state_space_causal_amd as ssm
+    from selective_state_space_causal_amd import inputs as I
+
+    w = I.AGGREGATES[args.codec]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ssm.load()
+    n, block, P = w.tokens * w.d_model, w.block, w.parts
+    es = 2 if w.io == "bf16" else 4
+    nb = ssm.q8_num_blocks(n, block)
+    log(f"bench: codec {w.name} tokens={w.tokens} d_model={w.d_model} parts={P} block={block} io={w.io}")
+    xs = [I.make_aggregate(w.tokens, w.d_model, w.io, seed=0, part=p, device=dev).reshape(-1) for p in range(P)]
+    qs = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(P)]
+    ss = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(P)]
+    for p in range(P):  # the parts "received" from the other ranks
+        ssm.q8_quantize(xs[p], block, q=qs[p], scales=ss[p])
+    y = torch.empty(n, dtype=xs[0].dtype, device=dev)
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("bench: copy calibration: 1 GiB read + 1 GiB written")
+        del src, dst
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(marks):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        ssm.q8_quantize(xs[0], block, q=qs[0], scales=ss[0], stream=stream)
+        e1.record(stream)
+        ssm.q8_dequant_sum(qs, ss, block, xs[0].dtype, y=y, stream=stream)
+        e2.record(stream)
+        marks.append((e0, e1, e2))
+
+    warm = []
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    marks = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(marks)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    q_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / len(marks)
+    d_ms = sum(b.elapsed_time(c) for _, b, c in marks) / len(marks)
+    qb, db = codec_bytes(n, nb, es, P)
+    q_gbps, d_gbps = qb / (q_ms * 1e-3) / 1e9, db / (d_ms * 1e-3) / 1e9
+    step_gbps = (qb + db) / ((q_ms + d_ms) * 1e-3) / 1e9
+    log(f"bench: quantize {q_ms * 1e3:.1f} us ({q_gbps:.0f} GB/s), dequant-sum of {P} parts {d_ms * 1e3:.1f} us "
+        f"({d_gbps:.0f} GB/s)")
+    rec = {
+        "metric": "int8 codec GB/s (quantize one rank's partial + dequant-sum of the parts; algorithmic bytes)",
+        "value": round(step_gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.tokens, "d_model": w.d_model, "parts": P, "block": block,
+                   "io": w.io, "parallelism": "none (the collective between ranks is not part of this build)"},
+        "quantize": {"us": round(q_ms * 1e3, 2), "algorithmic_bytes": qb, "achieved": round(q_gbps, 1),
+                     "frac": round(q_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(w.name, "quantize")},
+        "dequant_sum": {"us": round(d_ms * 1e3, 2), "algorithmic_bytes": db, "achieved": round(d_gbps, 1),
+                        "frac": round(d_gbps / HBM_PEAK_GBPS, 4),
+                        "traffic": traffic_from_profiles(w.name, "dequant_sum")},
+        "roofline": {"kernel": "dequant_sum", "bound": "hbm", "achieved": round(d_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(d_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profiles(w.name, "dequant_sum")},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the codec oracle on the host")
+        rec["cpu_baseline"] = codec_cpu_baseline(xs, block, n)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,11 +284,14 @@ def main():
     ap.add_argument("--pool", action="store_true",
                     help="serving form: ragged prompt lengths (uniform in [L/2, L]) and a cache pool of 2*batch "
                          "entries addressed through a random slot map (ssm_prefill_pool / ssm_decode_step_pool)")
+    ap.add_argument("--codec", metavar="AGGREGATE", default=None,
+                    help="instead of the scan, time the int8 codec on an aggregation-tensor workload "
+                         "(tp_prefill_7b or tp_decode_2.8b) and print its own JSON line")
     ap.add_argument("--record-traffic", metavar="PMC_DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs and exit")
     args = ap.parse_args()
     if args.record_traffic:
-        record_traffic(args.record_traffic, args.workload)
+        record_traffic(args.record_traffic, args.codec or args.workload)
         return
 
     if args.gpus != 1:
@@ -176,6 +299,10 @@ def main():
               "(the channel-local recurrence would shard by channel with no exchange inside it).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.codec:
+        bench_codec(args)
+        return
 
     import torch
 

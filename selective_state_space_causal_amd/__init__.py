@@ -1,9 +1,10 @@
 """MI355X-native selective state-space causal scan (prefill + decode) for one GPU's channel slice.
 
 ``prefill`` and ``decode_step`` call the C ABI of include/ssm.h (libssm.so, hand-written
-HIP kernels for gfx950) through a thin ctypes binding; ``inputs`` makes seeded synthetic
+HIP kernels for gfx950) through a thin ctypes binding; ``q8_quantize`` and
+``q8_dequant_sum`` call the block int8 codec of include/ssm_codec.h; ``inputs`` makes seeded synthetic
 workloads.  Importing the package does not load the library; the first call does, and
 raises if it is not built.
 """
 from ._lib import (SsmError, decode_step, decode_step_pool, load, prefill, prefill_pool,  # noqa: F401
-                   workspace_bytes)
+                   q8_dequant_sum, q8_num_blocks, q8_quantize, workspace_bytes)

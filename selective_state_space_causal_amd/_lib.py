@@ -68,6 +68,13 @@ def load(path: str = LIB_PATH):
     lib.ssm_decode_step_pool.restype = ctypes.c_int
     lib.ssm_decode_step_pool.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params)] + [vp] * 6 + [i64] + \
         [vp] * 4
+    lib.ssm_q8_num_blocks.restype = i64
+    lib.ssm_q8_num_blocks.argtypes = [i64, ctypes.c_int32]
+    lib.ssm_q8_quantize.restype = ctypes.c_int
+    lib.ssm_q8_quantize.argtypes = [i64, ctypes.c_int32, ctypes.c_int32] + [vp] * 4
+    lib.ssm_q8_dequant_sum.restype = ctypes.c_int
+    lib.ssm_q8_dequant_sum.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp]
     if lib.ssm_abi_version() != ABI_VERSION:
         raise ImportError(f"libssm ABI {lib.ssm_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -242,3 +249,56 @@ def decode_step_pool(x_t, dt_t, z_t, B_t, C_t, params: dict, slots, h_pool, conv
     if st != 0:
         raise SsmError("ssm_decode_step_pool", st, lib.ssm_status_str(st).decode())
     return y_t
+
+
+# ---- block int8 codec of include/ssm_codec.h ----
+
+Q8_MAX_PARTS = 16
+
+
+def q8_num_blocks(n: int, block: int) -> int:
+    """Scales per tensor of n elements: ceil(n / block) (0 for invalid arguments)."""
+    return int(load().ssm_q8_num_blocks(n, block))
+
+
+def q8_quantize(x, block: int = 128, *, q=None, scales=None, stream=None):
+    """x (any shape, contiguous, float32 or bfloat16, on the GPU) -> (q int8 [x.numel()],
+    scales float32 [ceil(numel / block)])."""
+    lib = load()
+    if x.device.type != "cuda" or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    n = x.numel()
+    nb = q8_num_blocks(n, block)
+    if q is None:
+        q = torch.empty(n, dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(max(nb, 1), dtype=torch.float32, device=x.device)
+    _check(q, "q", (n,), torch.int8, x.device)
+    _check(scales, "scales", (max(nb, 1),), torch.float32, x.device)
+    st = lib.ssm_q8_quantize(n, block, _io_code(x.dtype), _ptr(x), _ptr(q), _ptr(scales), stream_handle(stream))
+    if st != 0:
+        raise SsmError("ssm_q8_quantize", st, lib.ssm_status_str(st).decode())
+    return q, scales
+
+
+def q8_dequant_sum(q_parts, scale_parts, block: int = 128, dtype=torch.bfloat16, *, y=None, stream=None):
+    """Sum of the dequantized parts: y[i] = sum_p q_parts[p][i] * scale_parts[p][i // block]."""
+    lib = load()
+    parts = len(q_parts)
+    if parts != len(scale_parts) or parts < 1:
+        raise ValueError("q_parts and scale_parts must be non-empty lists of equal length")
+    n = q_parts[0].numel()
+    dev = q_parts[0].device
+    nb = q8_num_blocks(n, block)
+    for i in range(parts):
+        _check(q_parts[i], f"q_parts[{i}]", (n,), torch.int8, dev)
+        _check(scale_parts[i], f"scale_parts[{i}]", (max(nb, 1),), torch.float32, dev)
+    if y is None:
+        y = torch.empty(n, dtype=dtype, device=dev)
+    _check(y, "y", (n,), dtype, dev)
+    qa = (ctypes.c_void_p * parts)(*[t.data_ptr() for t in q_parts])
+    sa = (ctypes.c_void_p * parts)(*[t.data_ptr() for t in scale_parts])
+    st = lib.ssm_q8_dequant_sum(n, block, _io_code(dtype), parts, qa, sa, _ptr(y), stream_handle(stream))
+    if st != 0:
+        raise SsmError("ssm_q8_dequant_sum", st, lib.ssm_status_str(st).decode())
+    return y

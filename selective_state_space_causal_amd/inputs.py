@@ -141,3 +141,49 @@ def make_decode_token(batch: int, d_inner: int, d_state: int, step: int, io: str
     return {"x": s["x"][..., 0].contiguous(), "dt": s["dt"][..., 0].contiguous(),
             "z": s["z"][..., 0].contiguous(), "Bm": s["Bm"][:, 0].contiguous(),
             "Cm": s["Cm"][:, 0].contiguous()}
+
+
+# ---- the tensor-parallel aggregation tensor (input of the int8 codec) ----
+#
+# Under tensor parallelism each rank's slice of the mixer ends in a partial output
+# [tokens, d_model] that the ranks sum (page 1, Methodology item 4).  Stand-in recipe:
+# every element N(0, 1) times a per-token magnitude log-uniform in [1e-2, 1e2], so blocks
+# along d_model see scales that differ by orders of magnitude from token to token.  Each
+# rank's part has its own stream.
+
+@dataclass(frozen=True)
+class AggregateWorkload:
+    name: str
+    tokens: int
+    d_model: int
+    parts: int                   # tensor-parallel ranks whose parts are summed
+    block: int                   # elements per int8 scale
+    io: str
+    note: str = ""
+
+
+AGGREGATES = {
+    "tp_prefill_7b": AggregateWorkload("tp_prefill_7b", 32768, 4096, 4, 128, "bf16",
+                                       note="7B-class layer (d_model 4096), 32K-token prefill, 4 ranks"),
+    "tp_decode_2.8b": AggregateWorkload("tp_decode_2.8b", 64, 2560, 4, 128, "bf16",
+                                        note="Mamba-2.8B-shaped layer (d_model 2560), one decode token for "
+                                             "a batch of 64, 4 ranks"),
+}
+
+
+def make_aggregate(tokens: int, d_model: int, io: str = "bf16", seed: int = 0, part: int = 0,
+                   device="cpu") -> torch.Tensor:
+    """One rank's partial output [tokens, d_model] (recipe above), drawn with torch's RNG on
+    `device` (values depend on the device's generator; seeded and reproducible)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(seed, "aggregate", part))
+    mag = torch.exp(torch.empty(tokens, 1, device=device).uniform_(float(np.log(1e-2)), float(np.log(1e2)),
+                                                                    generator=g))
+    out = torch.empty(tokens, d_model, dtype=io_dtype(io), device=device)
+    rows = max(1, (1 << 24) // d_model)  # bound the fp32 temporary
+    for r0 in range(0, tokens, rows):
+        r1 = min(tokens, r0 + rows)
+        t = torch.randn(r1 - r0, d_model, generator=g, device=device, dtype=torch.float32)
+        out[r0:r1].copy_(t.mul_(mag[r0:r1]))
+        del t
+    return out
