@@ -98,8 +98,10 @@ def record_traffic(pmc_dir, workload):
             vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
         per[ctr] = vals
     gib_kib = float(1 << 20)
-    # the calibration copy is the only dispatch that writes a full GiB
-    copy_name = max(per["WRITE_SIZE"], key=lambda k: max(per["WRITE_SIZE"][k]))
+    # The calibration copy is the device-to-device copy dispatch that writes a full GiB (the
+    # fill that initialises its source writes a GiB too but reads nothing).
+    copies = [k for k in per["WRITE_SIZE"] if "copyBuffer" in k] or list(per["WRITE_SIZE"])
+    copy_name = max(copies, key=lambda k: max(per["WRITE_SIZE"][k]) + max(per["FETCH_SIZE"].get(k, [0.0])))
     wi = per["WRITE_SIZE"][copy_name].index(max(per["WRITE_SIZE"][copy_name]))
     fetch_scale = gib_kib / per["FETCH_SIZE"][copy_name][wi]
     write_scale = gib_kib / per["WRITE_SIZE"][copy_name][wi]
