@@ -9,10 +9,10 @@
 // 16-byte bf16 load, two fp32 ones), so a block of 32 / 64 / 128 / 256 elements spans
 // 4 / 8 / 16 / 32 lanes of one wave: its |x| maximum is reduced in registers with DPP
 // (quad swaps, then the half-row and row mirrors) and, for 32 lanes, one ds_swizzle.  A
-// workgroup covers 2048 elements, a whole number of blocks, and addresses its slice through
-// raw buffer descriptors whose range ends at the tensor's end: a lane past the end reads
-// zeros, its stores are dropped, and the one lane that straddles the end uses element
-// accesses.
+// workgroup works on tiles of 2048 elements, a whole number of blocks (quantize: one tile per
+// workgroup; dequant-sum: a grid-stride loop), and addresses each tile through raw buffer
+// descriptors whose range ends at the tensor's end: a lane past the end reads zeros, its
+// stores are dropped, and the one lane that straddles the end uses element accesses.
 #include <string.h>
 
 #include "../../include/ssm_codec.h"
@@ -29,6 +29,7 @@ constexpr float QMAX = 127.0f;
 // (the codes written by quantize, the codes read and the sum written by dequant-sum); it
 // measured 3-8% faster on those and slower on quantize's input loads.
 constexpr int NT = 2;
+constexpr int64_t DEQUANT_MAX_GRID = 4096;  // 16 workgroups per CU
 
 struct QuantArgs {
   const void* x;
@@ -135,10 +136,9 @@ __global__ __launch_bounds__(TPB) void q8_quantize(QuantArgs a) {
   if (threadIdx.x % LPB == 0 && first < cnt) a.scales[e0 / BLOCK + threadIdx.x / LPB] = scale;
 }
 
-template <typename IO, int BLOCK>
-__global__ __launch_bounds__(TPB) void q8_dequant_sum(DequantArgs a) {
-  constexpr int LPB = BLOCK / EPL;
-  const int64_t e0 = (int64_t)blockIdx.x * EPW;
+// One 2048-element tile of dequant-sum: elements [e0, e0 + 2048) of every part.
+template <typename IO, int BLOCK, int LPB>
+__device__ __forceinline__ void dequant_tile(const DequantArgs& a, int64_t e0) {
   const int64_t left = a.n - e0;
   const int cnt = left < EPW ? (int)left : EPW;
   const int nbw = (cnt + BLOCK - 1) / BLOCK;  // scales of this workgroup
@@ -198,9 +198,19 @@ __global__ __launch_bounds__(TPB) void q8_dequant_sum(DequantArgs a) {
   }
 }
 
-// One instantiation per (io dtype, block size); KERNEL is q8_quantize or q8_dequant_sum.
-#define SSM_Q8_DISPATCH(KERNEL)                                                        \
-  const dim3 grid((unsigned)((n + EPW - 1) / EPW)), tb(TPB);                           \
+// Grid-stride over 2048-element tiles (the grid is capped at DEQUANT_MAX_GRID workgroups):
+// measured 7% faster than one tile per workgroup.
+template <typename IO, int BLOCK>
+__global__ __launch_bounds__(TPB) void q8_dequant_sum(DequantArgs a) {
+  constexpr int LPB = BLOCK / EPL;
+  for (int64_t e0 = (int64_t)blockIdx.x * EPW; e0 < a.n; e0 += (int64_t)gridDim.x * EPW)
+    dequant_tile<IO, BLOCK, LPB>(a, e0);
+}
+
+// One instantiation per (io dtype, block size); KERNEL is q8_quantize or q8_dequant_sum,
+// launched on GRID workgroups.
+#define SSM_Q8_DISPATCH(KERNEL, GRID)                                                  \
+  const dim3 grid((unsigned)(GRID)), tb(TPB);                                          \
   const bool bf = io_dtype == SSM_BF16;                                                \
   switch (block) {                                                                     \
     case 32:                                                                           \
@@ -223,11 +233,13 @@ __global__ __launch_bounds__(TPB) void q8_dequant_sum(DequantArgs a) {
   return hipGetLastError();
 
 hipError_t launch_quantize(int io_dtype, int block, int64_t n, const QuantArgs& a, hipStream_t s) {
-  SSM_Q8_DISPATCH(q8_quantize)
+  SSM_Q8_DISPATCH(q8_quantize, (n + EPW - 1) / EPW)
 }
 
 hipError_t launch_dequant_sum(int io_dtype, int block, int64_t n, const DequantArgs& a, hipStream_t s) {
-  SSM_Q8_DISPATCH(q8_dequant_sum)
+  const int64_t tiles = (n + EPW - 1) / EPW;
+  const int64_t grid_tiles = tiles < DEQUANT_MAX_GRID ? tiles : DEQUANT_MAX_GRID;
+  SSM_Q8_DISPATCH(q8_dequant_sum, grid_tiles)
 }
 #undef SSM_Q8_DISPATCH
 
