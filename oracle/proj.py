@@ -1,0 +1,74 @@
+"""Channel-sliced projections either side of the scan, and the conv front on its own:
+plain CPU oracle (numpy, fp64).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It shares no code with the GPU library.
+
+What it follows: "Scaling State-Space Models on Multiple GPUs with Tensor Parallelism"
+(euno.news summary of arXiv 2602.21144), Methodology item 1: the mixer's packed weight
+tensor (its long-range projections and its local mixing kernels) is split across GPUs along
+the feature dimension, as in Transformer tensor parallelism, while item 2 keeps the
+recurrence local.  One GPU therefore holds a column shard of the input projection (its own
+channels of x and z), the rows of the projection that makes the step sizes and B / C that
+read its channels (a partial sum over channels), the step-size projection of its own
+channels, and a row shard of the output projection (a partial sum that the ranks add).
+The pages do not write these maps; the Mamba mixer's (Gu & Dao, 2023) are used, in this
+library's layouts:
+  in_proj   out[b, c, t] = sum_k W[c, k] hidden[b, t, k]    W [D, d_model], out [B, D, L]
+  x_proj    out[b, t, j] = sum_c W[j, c] u[b, c, t]         W [J, D],       out [B, L, J]
+  dt_proj   out[b, c, t] = sum_r W[c, r] lowrank[b, t, r]   W [D, R],       out [B, D, L]
+  out_proj  out[b, t, m] = sum_c W[m, c] y[b, c, t]         W [d_model, D], out [B, L, d_model]
+  conv_silu u[b, c, t] = silu(conv_b[c] + sum_k conv_w[c, k] xi[b, c, t - 3 + k])
+(xi = the raw x, with history xi[-3..-1] = conv0 or zeros).  Each function takes the same
+io bits the GPU reads (widened exactly to fp64) and returns fp64.  Each projection is one
+library matrix product (numpy einsum) with no blocking or reordering.
+
+Pins: tests/proj_pins.py (torch conv1d in fp64, tap special cases, resume invariance, brute
+force triple loops on small sizes with all dimensions distinct, identity weights,
+linearity), with planted mistakes in tests/test_proj_mutants.py.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # torch tensor (any dtype, any device)
+        a = a.detach().to("cpu").double().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def in_proj(hidden, w) -> np.ndarray:
+    """hidden [B, L, d_model], W [D, d_model] -> [B, D, L]."""
+    return np.einsum("blk,ck->bcl", _f64(hidden), _f64(w))
+
+
+def x_proj(u, w) -> np.ndarray:
+    """u [B, D, L], W [J, D] -> [B, L, J] (this slice's partial sum over channels)."""
+    return np.einsum("bcl,jc->blj", _f64(u), _f64(w))
+
+
+def dt_proj(lowrank, w) -> np.ndarray:
+    """lowrank [B, L, R], W [D, R] -> [B, D, L]."""
+    return np.einsum("blr,cr->bcl", _f64(lowrank), _f64(w))
+
+
+def out_proj(y, w) -> np.ndarray:
+    """y [B, D, L], W [d_model, D] -> [B, L, d_model] (this slice's partial sum)."""
+    return np.einsum("bcl,mc->blm", _f64(y), _f64(w))
+
+
+def conv_silu(x, conv_w, conv_b=None, conv0: Optional[np.ndarray] = None) -> np.ndarray:
+    """x [B, D, L], conv_w [D, 4], conv_b [D] or None, conv0 [B, D, 3] or None -> u [B, D, L]."""
+    x = _f64(x)
+    B, D, L = x.shape
+    w = _f64(conv_w)
+    hist = np.zeros((B, D, 3)) if conv0 is None else _f64(conv0)
+    xi = np.concatenate([hist, x], axis=2)          # xi[..., s] = raw input at token s - 3
+    v = np.zeros((B, D, L)) if conv_b is None else np.broadcast_to(_f64(conv_b)[None, :, None], (B, D, L)).copy()
+    for k in range(4):                               # tap k multiplies the input at t - 3 + k
+        v = v + w[None, :, k, None] * xi[:, :, k:k + L]
+    with np.errstate(over="ignore"):                 # e^-v = inf gives the limit -0
+        return v / (1.0 + np.exp(-v))
