@@ -1,0 +1,91 @@
+/*
+ * ssm_proj.h -- C ABI of the channel-sliced projections on either side of the scan, and of
+ * the conv front on its own, on AMD Instinct MI355X (gfx950).  Part of libssm.so.
+ *
+ * The operation.  "Scaling State-Space Models on Multiple GPUs with Tensor Parallelism"
+ * (euno.news summary of arXiv 2602.21144), Methodology item 1: the mixer's packed weight
+ * tensor (long-range projections and local mixing kernels) is split across GPUs along the
+ * feature dimension, as Transformer tensor parallelism splits its matrices, while item 2 keeps
+ * the token-by-token recurrence on each GPU.  A GPU holding channels [c0, c0 + D) of the
+ * mixer therefore runs, around the scan of ssm.h:
+ *   in_proj   its column shard of the input projection: hidden -> its x and z channels;
+ *   conv      the causal conv + SiLU front alone, u = silu(conv(x)), the input of x_proj;
+ *   x_proj    the rows of the projection that reads its channels of u and makes the
+ *             low-rank step input, B and C: a partial sum over channels, which the ranks add;
+ *   dt_proj   the step-size projection of its own channels;
+ *   out_proj  its row shard of the output projection: a partial sum, which the ranks add
+ *             (the quantized all-reduce of ssm_codec.h).
+ * The pages do not write these maps; this library uses the Mamba mixer's (Gu & Dao, 2023).
+ *
+ * The four projections are dense contractions and run as bf16 (or fp32) GEMMs with fp32
+ * accumulation on the matrix cores through hipBLASLt (a plain library GEMM, no fusion);
+ * this library supplies the layouts, so that each projection reads and writes the scan's
+ * tensors in place:
+ *   kind SSM_PROJ_IN / SSM_PROJ_DT (token-major in, channel-major out):
+ *       out[b, m, t] = sum_k W[m, k] * in[b, t, k]     in [B, L, K], W [M, K], out [B, M, L]
+ *   kind SSM_PROJ_X / SSM_PROJ_OUT (channel-major in, token-major out):
+ *       out[b, t, m] = sum_k W[m, k] * in[b, k, t]     in [B, K, L], W [M, K], out [B, L, M]
+ * (B = batch, L = seqlen, K = in_features, M = out_features; every tensor row-major and
+ * contiguous.)  in_proj is called once for x (W = the x rows) and once for z; x_proj once per
+ * output group (low-rank step input, B, C) so that each lands in its own contiguous tensor.
+ *
+ * Conventions (as in ssm.h): device pointers owned by the caller; calls are stream-ordered
+ * and asynchronous; arguments are validated on the host first, and an invalid call returns a
+ * non-zero ssm_status and enqueues nothing.  A projection context holds a hipBLASLt handle
+ * and a cache of the algorithms chosen per shape: create one per host thread (a context is
+ * not safe for concurrent use); it allocates host memory only.  Device scratch comes from the
+ * caller (ssm_proj_workspace_bytes).
+ */
+#ifndef SSM_PROJ_H
+#define SSM_PROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ssm_proj_ctx ssm_proj_ctx;
+
+typedef enum { SSM_PROJ_IN = 0, SSM_PROJ_X = 1, SSM_PROJ_DT = 2, SSM_PROJ_OUT = 3 } ssm_proj_kind;
+
+/* Create / destroy a projection context.  create returns SSM_ERR_NULL for a NULL out-pointer
+ * and SSM_ERR_LAUNCH when hipBLASLt cannot be initialised. */
+int ssm_proj_create(ssm_proj_ctx** ctx);
+void ssm_proj_destroy(ssm_proj_ctx* ctx);
+
+/* Device workspace a projection call may use; pass at least this much to ssm_proj. */
+size_t ssm_proj_workspace_bytes(void);
+
+/*
+ * One projection (layouts above).  io_dtype (SSM_BF16 or SSM_F32) types `in` and `w`;
+ * out_dtype types `out` (a partial sum may be kept in fp32).  All sizes >= 1.  Alignment:
+ * every pointer 16-byte.  out may not overlap in or w.
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE (a size < 1, a kind out of range, sizes that overflow),
+ * SSM_ERR_DTYPE, SSM_ERR_ALIGN, SSM_ERR_ALIAS, SSM_ERR_WORKSPACE (workspace NULL or smaller
+ * than ssm_proj_workspace_bytes()), SSM_ERR_LAUNCH (hipBLASLt found no algorithm or failed).
+ * Passage: Methodology items 1-2 of the page cited above.
+ */
+int ssm_proj(ssm_proj_ctx* ctx, int32_t kind, int64_t batch, int64_t seqlen, int64_t in_features,
+             int64_t out_features, int32_t io_dtype, int32_t out_dtype, const void* in, const void* w, void* out,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Conv front alone: u[b, c, t] = silu(conv_b[c] + sum_k conv_w[c, k] * xi[b, c, t - 3 + k]),
+ * with xi the raw x and xi[-3..-1] = conv0[b, c, 0..2] (NULL = zeros), in the io dtype
+ * (bf16: round to nearest even).  The same arithmetic, in the same order, as the front end
+ * inside ssm_prefill.  Uses dims (batch, seqlen, d_inner, d_conv = 4, io_dtype) and
+ * params->conv_w / conv_b only.  Alignment: x and u 16-byte, conv_w 16-byte, conv_b and conv0
+ * 4-byte.  u may not overlap x.
+ * Passage: the local mixing kernels of Methodology item 1 of the page cited above.
+ */
+int ssm_conv_silu(const ssm_dims* dims, const ssm_params* params, const void* x, const float* conv0, void* u,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_PROJ_H */

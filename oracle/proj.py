@@ -72,3 +72,34 @@ def conv_silu(x, conv_w, conv_b=None, conv0: Optional[np.ndarray] = None) -> np.
         v = v + w[None, :, k, None] * xi[:, :, k:k + L]
     with np.errstate(over="ignore"):                 # e^-v = inf gives the limit -0
         return v / (1.0 + np.exp(-v))
+
+
+def to_io(a, io: str) -> np.ndarray:
+    """Round fp64 values to the io dtype the GPU stores a tensor in (bf16: through fp32, each
+    step round to nearest even), returned widened to fp64."""
+    import torch  # test infrastructure; torch's casts are round-to-nearest-even
+
+    t = torch.from_numpy(np.asarray(a, dtype=np.float64)).to(torch.float32)
+    if io == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.double().numpy()
+
+
+def layer_prefill(hidden, w: dict, params: dict, io: str = "bf16", nthreads: int = 1):
+    """One rank's mixer layer over a prompt, as the library composes it: in_proj (x, z),
+    conv front, x_proj (low-rank step input, B, C), dt_proj, the scan (the C oracle), and
+    out_proj as an fp32 partial; every intermediate tensor the GPU stores in the io dtype is
+    rounded to it here at the same point.  Returns (out [B, L, d_model] fp64, h, conv)."""
+    from . import prefill as scan_prefill  # the fp64 C oracle of the scan
+
+    x = to_io(in_proj(hidden, w["in_x"]), io)
+    z = to_io(in_proj(hidden, w["in_z"]), io)
+    u = to_io(conv_silu(x, params["conv_w"], params.get("conv_b")), io)
+    lowrank = to_io(x_proj(u, w["x_dt"]), io)
+    Bm = to_io(x_proj(u, w["x_B"]), io)
+    Cm = to_io(x_proj(u, w["x_C"]), io)
+    dt = to_io(dt_proj(lowrank, w["dt"]), io)
+    y, h, c = scan_prefill({"x": x, "dt": dt, "z": z, "Bm": Bm, "Cm": Cm},
+                           {k: _f64(v) for k, v in params.items() if v is not None}, nthreads=nthreads)
+    y = to_io(y, io)
+    return out_proj(y, w["out"]), h, c

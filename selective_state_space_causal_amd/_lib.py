@@ -75,6 +75,17 @@ def load(path: str = LIB_PATH):
     lib.ssm_q8_dequant_sum.restype = ctypes.c_int
     lib.ssm_q8_dequant_sum.argtypes = [i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp]
+    lib.ssm_proj_create.restype = ctypes.c_int
+    lib.ssm_proj_create.argtypes = [ctypes.POINTER(vp)]
+    lib.ssm_proj_destroy.restype = None
+    lib.ssm_proj_destroy.argtypes = [vp]
+    lib.ssm_proj_workspace_bytes.restype = sz
+    lib.ssm_proj_workspace_bytes.argtypes = []
+    lib.ssm_proj.restype = ctypes.c_int
+    lib.ssm_proj.argtypes = [vp, ctypes.c_int32, i64, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp,
+                             sz, vp]
+    lib.ssm_conv_silu.restype = ctypes.c_int
+    lib.ssm_conv_silu.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params), vp, vp, vp, vp]
     if lib.ssm_abi_version() != ABI_VERSION:
         raise ImportError(f"libssm ABI {lib.ssm_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -302,3 +313,77 @@ def q8_dequant_sum(q_parts, scale_parts, block: int = 128, dtype=torch.bfloat16,
     if st != 0:
         raise SsmError("ssm_q8_dequant_sum", st, lib.ssm_status_str(st).decode())
     return y
+
+
+# ---- channel-sliced projections and the conv front of include/ssm_proj.h ----
+
+PROJ_IN, PROJ_X, PROJ_DT, PROJ_OUT = 0, 1, 2, 3
+
+
+class Projector:
+    """A projection context (hipBLASLt handle + per-shape algorithm cache) with its device
+    workspace.  Layouts: IN / DT map token-major in [B, L, K] to channel-major out [B, M, L];
+    X / OUT map channel-major in [B, K, L] to token-major out [B, L, M]; W is [M, K]."""
+
+    def __init__(self, device="cuda"):
+        self.lib = load()
+        h = ctypes.c_void_p()
+        st = self.lib.ssm_proj_create(ctypes.byref(h))
+        if st != 0:
+            raise SsmError("ssm_proj_create", st, self.lib.ssm_status_str(st).decode())
+        self.handle = h
+        self.ws_bytes = int(self.lib.ssm_proj_workspace_bytes())
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            self.lib.ssm_proj_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __call__(self, kind: int, x, w, *, out=None, out_dtype=None, stream=None):
+        lib = self.lib
+        if kind not in (PROJ_IN, PROJ_X, PROJ_DT, PROJ_OUT):
+            raise ValueError(f"unknown projection kind {kind}")
+        M, K = w.shape
+        token_major_in = kind in (PROJ_IN, PROJ_DT)
+        if token_major_in:
+            Bn, L, K2 = x.shape
+        else:
+            Bn, K2, L = x.shape
+        if K2 != K:
+            raise ValueError(f"in_features mismatch: input has {K2}, weight has {K}")
+        out_dtype = x.dtype if out_dtype is None else out_dtype
+        shape = (Bn, M, L) if token_major_in else (Bn, L, M)
+        if out is None:
+            out = torch.empty(shape, dtype=out_dtype, device=x.device)
+        _check(x, "x", tuple(x.shape), x.dtype, x.device)
+        _check(w, "w", (M, K), x.dtype, x.device)
+        _check(out, "out", shape, out_dtype, x.device)
+        st = lib.ssm_proj(self.handle, kind, Bn, L, K, M, _io_code(x.dtype), _io_code(out_dtype), _ptr(x), _ptr(w),
+                          _ptr(out), _ptr(self.ws), self.ws_bytes, stream_handle(stream))
+        if st != 0:
+            raise SsmError("ssm_proj", st, lib.ssm_status_str(st).decode())
+        return out
+
+
+def conv_silu(x, params: dict, conv0=None, *, u=None, stream=None):
+    """u = silu(conv(x)) for x [B, D, L] (the scan's front end, materialised)."""
+    lib = load()
+    Bn, D, L = x.shape
+    if u is None:
+        u = torch.empty_like(x)
+    _check(u, "u", (Bn, D, L), x.dtype, x.device)
+    _check(conv0, "conv0", (Bn, D, CONV_W - 1), torch.float32, x.device, optional=True)
+    d = Dims(Bn, L, D, 1, CONV_W, _io_code(x.dtype), 0)
+    p = Params(None, None, None, params["conv_w"].data_ptr(),
+               None if params.get("conv_b") is None else params["conv_b"].data_ptr())
+    st = lib.ssm_conv_silu(ctypes.byref(d), ctypes.byref(p), _ptr(x), _ptr(conv0), _ptr(u), stream_handle(stream))
+    if st != 0:
+        raise SsmError("ssm_conv_silu", st, lib.ssm_status_str(st).decode())
+    return u

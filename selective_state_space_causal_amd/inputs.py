@@ -187,3 +187,63 @@ def make_aggregate(tokens: int, d_model: int, io: str = "bf16", seed: int = 0, p
         out[r0:r1].copy_(t.mul_(mag[r0:r1]))
         del t
     return out
+
+
+# ---- the channel-sliced projections around the scan (one rank's shard of a mixer layer) ----
+#
+# Page 1 (Methodology item 1) splits the mixer's projection weights across GPUs along the
+# feature dimension.  Stand-in weights for one rank's shard, random-initialised at the usual
+# 1/sqrt(fan_in) scale (no trained weights are used):
+#   in_x, in_z [D, d_model]      N(0, 1/d_model)   column shard of the input projection
+#   x_dt [R, D], x_B [N, D], x_C [N, D]  N(0, 1/D)  the rows of x_proj that read these channels
+#   dt [D, R]                    N(0, 1/R) * 0.5   step-size projection of these channels
+#   out [d_model, D]             N(0, 1/D)         row shard of the output projection
+# and the layer input hidden [B, L, d_model] ~ N(0, 1).  io tensors are rounded to bf16 (RNE).
+
+@dataclass(frozen=True)
+class LayerWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    d_model: int
+    d_inner: int                 # this rank's channels
+    dt_rank: int
+    d_state: int
+    io: str
+    note: str = ""
+
+
+LAYERS = {
+    "layer7b": LayerWorkload("layer7b", 1, 32768, 4096, 2048, 256, 16, "bf16",
+                             note="7B-class mixer layer (d_model 4096, d_inner 8192 split 4 ways), 32K-token "
+                                  "prefill: this rank's projections, conv front, scan"),
+    "layer_small": LayerWorkload("layer_small", 2, 200, 96, 64, 8, 16, "bf16",
+                                 note="small layer the oracle runs in seconds"),
+}
+
+
+def make_proj_weights(d_model: int, d_inner: int, dt_rank: int, d_state: int, io: str = "bf16", seed: int = 0,
+                      device="cpu") -> dict:
+    dtype = io_dtype(io)
+
+    def normal(name, shape, std):
+        g = torch.Generator(device=device)
+        g.manual_seed(torch_seed(seed, "proj", name))
+        return (torch.randn(shape, generator=g, device=device) * std).to(dtype)
+
+    return {"in_x": normal("in_x", (d_inner, d_model), d_model ** -0.5),
+            "in_z": normal("in_z", (d_inner, d_model), d_model ** -0.5),
+            "x_dt": normal("x_dt", (dt_rank, d_inner), d_inner ** -0.5),
+            "x_B": normal("x_B", (d_state, d_inner), d_inner ** -0.5),
+            "x_C": normal("x_C", (d_state, d_inner), d_inner ** -0.5),
+            "dt": normal("dt", (d_inner, dt_rank), 0.5 * dt_rank ** -0.5),
+            "out": normal("out", (d_model, d_inner), d_inner ** -0.5)}
+
+
+def make_hidden(batch: int, seqlen: int, d_model: int, io: str = "bf16", seed: int = 0, device="cpu") -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(seed, "hidden"))
+    out = torch.empty(batch, seqlen, d_model, dtype=io_dtype(io), device=device)
+    for b in range(batch):
+        out[b].copy_(torch.randn(seqlen, d_model, generator=g, device=device))
+    return out

@@ -1,0 +1,143 @@
+"""Channel-sliced projections, the conv front and one rank's mixer layer on the GPU against the
+fp64 oracle (oracle/proj.py, and the scan's C oracle for the layer).
+
+Projections: the GPU accumulates in fp32 (hipBLASLt, order unknown), so each output is held
+to |gpu - ref| <= K * 2^-24 * sum_k |W_mk in_k| (the worst case of any fp32 summation order)
+plus, for bf16 output, the final round to nearest even (at most 2^-8 of the value).  The conv
+front: fp32 arithmetic then the io rounding.  The layer: the oracle rounds every intermediate
+tensor to the io dtype at the same points as the GPU, and the output is held to the scan's
+tolerance, 2e-2 (1 + |ref|) for bf16 io."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import proj as P
+from selective_state_space_causal_amd import _lib as L
+from selective_state_space_causal_amd import inputs as I
+from selective_state_space_causal_amd import layer
+from tests.gpu_common import DEV, note, threads
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+REF = {L.PROJ_IN: P.in_proj, L.PROJ_DT: P.dt_proj, L.PROJ_X: P.x_proj, L.PROJ_OUT: P.out_proj}
+NAMES = {L.PROJ_IN: "in", L.PROJ_X: "x", L.PROJ_DT: "dt", L.PROJ_OUT: "out"}
+
+
+@pytest.fixture(scope="module")
+def pj():
+    p = L.Projector(DEV)
+    yield p
+    p.close()
+
+
+def bound(kind, x, w, ref, out_bf16):
+    K = w.shape[1]
+    mag = REF[kind](np.abs(x.double().numpy()), np.abs(w.double().numpy()))
+    b = K * U * mag
+    if out_bf16:
+        b = b + 2.0 ** -8 * (np.abs(ref) + b)
+    return b
+
+
+@pytest.mark.parametrize("kind", [L.PROJ_IN, L.PROJ_X, L.PROJ_DT, L.PROJ_OUT])
+@pytest.mark.parametrize("io,od", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
+@pytest.mark.parametrize("B,Ls,K,M", [(2, 64, 32, 48), (1, 33, 17, 5), (3, 7, 3, 9), (2, 520, 96, 40)])
+def test_projection_matches_oracle(pj, kind, io, od, B, Ls, K, M):
+    note(f"proj {NAMES[kind]} io={io} out={od} B={B} L={Ls} K={K} M={M}")
+    g = torch.Generator().manual_seed(B * 1000 + Ls * 10 + K + kind)
+    tm = kind in (L.PROJ_IN, L.PROJ_DT)
+    x = torch.randn((B, Ls, K) if tm else (B, K, Ls), generator=g).to(DT[io])
+    w = (torch.randn(M, K, generator=g) / K ** 0.5).to(DT[io])
+    out = pj(kind, x.to(DEV), w.to(DEV), out_dtype=DT[od])
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == ((B, M, Ls) if tm else (B, Ls, M))
+    ref = REF[kind](x, w)
+    got = out.double().cpu().numpy()
+    b = bound(kind, x, w, ref, od == "bf16")
+    err = np.abs(got - ref)
+    i = np.unravel_index(int(np.argmax(err - b)), err.shape)
+    assert np.all(err <= b), f"{i}: gpu {got[i]!r} ref {ref[i]!r} bound {b[i]:.3e}"
+
+
+def test_projection_errors(pj):
+    x = torch.randn(1, 64, 32, device=DEV, dtype=torch.bfloat16)
+    w = torch.randn(16, 32, device=DEV, dtype=torch.bfloat16)
+    buf = torch.empty(16 * 64 + 8, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(L.SsmError) as e:
+        pj(L.PROJ_IN, x, w, out=buf[1:1 + 16 * 64].view(1, 16, 64))   # 2-byte offset: not 16-byte aligned
+    assert e.value.status == 4
+    with pytest.raises(ValueError):
+        pj(L.PROJ_IN, x, torch.randn(16, 31, device=DEV, dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("B,D,Ls", [(2, 8, 64), (1, 5, 37), (2, 3, 1), (3, 16, 200), (1, 4, 12)])
+@pytest.mark.parametrize("resume", [False, True])
+def test_conv_silu_matches_oracle(io, B, D, Ls, resume):
+    note(f"conv_silu io={io} B={B} D={D} L={Ls} resume={resume}")
+    prm = I.make_params(D, 16)
+    g = torch.Generator().manual_seed(B * 100 + D * 10 + Ls)
+    x = torch.randn(B, D, Ls, generator=g).to(DT[io])
+    conv0 = torch.randn(B, D, 3, generator=g).to(DT[io]).float() if resume else None
+    pd = {k: v.to(DEV) for k, v in prm.items() if v is not None}
+    u = L.conv_silu(x.to(DEV), pd, None if conv0 is None else conv0.to(DEV))
+    torch.cuda.synchronize()
+    ref = P.conv_silu(x, prm["conv_w"], prm.get("conv_b"), None if conv0 is None else conv0.double().numpy())
+    got = u.double().cpu().numpy()
+    tol = 2.0 ** -8 * np.abs(ref) + 1e-6 * (1 + np.abs(ref)) if io == "bf16" else 2e-6 * (1 + np.abs(ref))
+    assert np.all(np.abs(got - ref) <= tol), float(np.max(np.abs(got - ref) - tol))
+
+
+def test_conv_silu_resume_is_bitwise():
+    """Running tokens [L1, L) with the last three raw inputs before L1 as history reproduces
+    the tail of the full run bit for bit (the arithmetic per token is the same)."""
+    prm = {k: v.to(DEV) for k, v in I.make_params(12, 16).items() if v is not None}
+    x = torch.randn(2, 12, 96, device=DEV).to(torch.bfloat16)
+    full = L.conv_silu(x, prm)
+    for L1 in (8, 40, 88):
+        hist = x[:, :, L1 - 3:L1].float().contiguous()
+        tail = L.conv_silu(x[:, :, L1:].contiguous(), prm, hist)
+        torch.cuda.synchronize()
+        assert torch.equal(tail, full[:, :, L1:]), L1
+
+
+def test_layer_small_matches_oracle(pj):
+    w8 = I.LAYERS["layer_small"]
+    note(f"layer {w8}")
+    prm = I.make_params(w8.d_inner, w8.d_state)
+    wts = I.make_proj_weights(w8.d_model, w8.d_inner, w8.dt_rank, w8.d_state, w8.io)
+    hidden = I.make_hidden(w8.batch, w8.seqlen, w8.d_model, w8.io)
+    out, h, c = layer.mixer_prefill(hidden.to(DEV), {k: v.to(DEV) for k, v in wts.items()},
+                                    {k: v.to(DEV) for k, v in prm.items() if v is not None}, pj)
+    torch.cuda.synchronize()
+    ref, h_ref, c_ref = P.layer_prefill(hidden, wts, prm, w8.io, nthreads=threads())
+    got = out.double().cpu().numpy()
+    err = np.abs(got - ref) / (1 + np.abs(ref))
+    note(f"layer: max err {err.max():.3e}")
+    assert err.max() <= 2e-2
+    herr = np.abs(h.double().cpu().numpy() - h_ref) / (1 + np.abs(h_ref))
+    assert herr.max() <= 2e-2
+
+
+def test_in_proj_full_size_sampled(pj):
+    """in_proj of the 7B-class layer at its real size ([1, 32768, 4096] x [2048, 4096], bf16):
+    sampled outputs against fp64 dot products."""
+    w8 = I.LAYERS["layer7b"]
+    hidden = I.make_hidden(w8.batch, w8.seqlen, w8.d_model, w8.io, device=DEV)
+    wx = I.make_proj_weights(w8.d_model, w8.d_inner, w8.dt_rank, w8.d_state, w8.io, device=DEV)["in_x"]
+    x = pj(L.PROJ_IN, hidden, wx)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(0)
+    cs = g.integers(0, w8.d_inner, 400)
+    ts = g.integers(0, w8.seqlen, 400)
+    hs = hidden[0, torch.tensor(ts, device=DEV)].double().cpu().numpy()   # [400, d_model]
+    ws = wx[torch.tensor(cs, device=DEV)].double().cpu().numpy()
+    ref = np.sum(hs * ws, axis=1)
+    mag = np.sum(np.abs(hs * ws), axis=1)
+    got = x[0, torch.tensor(cs, device=DEV), torch.tensor(ts, device=DEV)].double().cpu().numpy()
+    b = w8.d_model * U * mag
+    b = b + 2.0 ** -8 * (np.abs(ref) + b)
+    assert np.all(np.abs(got - ref) <= b)
