@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD public specification
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, AMD public specification
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, AMD public specification
 CONV_W = 4
 
@@ -270,6 +271,117 @@ def bench_codec(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_layer(args):
+    """One step = one rank's mixer layer over the prompt: in_proj (x, z), conv front, x_proj
+    (low-rank step input, B, C), dt_proj, the scan, out_proj (fp32 partial)."""
+    import torch
+
+    import selective_state_space_causal_amd as ssm
+    from selective_state_space_causal_amd import inputs as I
+
+    w = I.LAYERS[args.layer]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ssm.load()
+    B, L, DM, D, R, N = w.batch, w.seqlen, w.d_model, w.d_inner, w.dt_rank, w.d_state
+    log(f"bench: layer {w.name} B={B} L={L} d_model={DM} d_inner={D} dt_rank={R} d_state={N} io={w.io}")
+    prm = {k: v.to(dev) for k, v in I.make_params(D, N).items() if v is not None}
+    wts = I.make_proj_weights(DM, D, R, N, w.io, device=dev)
+    hidden = I.make_hidden(B, L, DM, w.io, device=dev)
+    pj = ssm.Projector(dev)
+    dt_ = hidden.dtype
+    x = torch.empty(B, D, L, dtype=dt_, device=dev)
+    z, u, dtt = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    lowrank = torch.empty(B, L, R, dtype=dt_, device=dev)
+    Bm, Cm = torch.empty(B, L, N, dtype=dt_, device=dev), torch.empty(B, L, N, dtype=dt_, device=dev)
+    y = torch.empty_like(x)
+    h = torch.empty(B, D, N, dtype=torch.float32, device=dev)
+    c = torch.empty(B, D, CONV_W - 1, dtype=torch.float32, device=dev)
+    out = torch.empty(B, L, DM, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["in_proj_x", "in_proj_z", "conv_silu", "x_proj_dt", "x_proj_B", "x_proj_C", "dt_proj", "scan", "out_proj"]
+
+    def stages():
+        yield lambda: pj(ssm.PROJ_IN, hidden, wts["in_x"], out=x, stream=stream)
+        yield lambda: pj(ssm.PROJ_IN, hidden, wts["in_z"], out=z, stream=stream)
+        yield lambda: ssm.conv_silu(x, prm, u=u, stream=stream)
+        yield lambda: pj(ssm.PROJ_X, u, wts["x_dt"], out=lowrank, stream=stream)
+        yield lambda: pj(ssm.PROJ_X, u, wts["x_B"], out=Bm, stream=stream)
+        yield lambda: pj(ssm.PROJ_X, u, wts["x_C"], out=Cm, stream=stream)
+        yield lambda: pj(ssm.PROJ_DT, lowrank, wts["dt"], out=dtt, stream=stream)
+        yield lambda: ssm.prefill(x, dtt, z, Bm, Cm, prm, y=y, h_out=h, conv_out=c, stream=stream)
+        yield lambda: pj(ssm.PROJ_OUT, y, wts["out"], out=out, stream=stream)
+
+    def step(marks):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        evs[0].record(stream)
+        for i, f in enumerate(stages()):
+            f()
+            evs[i + 1].record(stream)
+        marks.append(evs)
+
+    warm = []
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    marks = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(marks)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = [sum(m[i].elapsed_time(m[i + 1]) for m in marks) / len(marks) for i in range(len(names))]
+    total = sum(ms)
+    tokens = B * L
+    flops = {"in_proj_x": 2 * tokens * DM * D, "in_proj_z": 2 * tokens * DM * D, "x_proj_dt": 2 * tokens * D * R,
+             "x_proj_B": 2 * tokens * D * N, "x_proj_C": 2 * tokens * D * N, "dt_proj": 2 * tokens * R * D,
+             "out_proj": 2 * tokens * D * DM}
+    stages_rec = {}
+    for n, t in zip(names, ms):
+        e = {"ms": round(t, 4)}
+        if n in flops:
+            tf = flops[n] / (t * 1e-3) / 1e12
+            e.update({"tflops": round(tf, 1), "mfma_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)})
+        stages_rec[n] = e
+    log("bench: " + ", ".join(f"{n} {t * 1e3:.1f} us" for n, t in zip(names, ms)) + f"; layer {total:.3f} ms")
+    gemm = stages_rec["in_proj_x"]
+    rec = {
+        "metric": "mixer layer tokens/s (one rank's channel slice: projections, conv front, scan)",
+        "value": round(tokens / (total * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (random-init weights)",
+        "config": {"workload": w.name, "batch": B, "seqlen": L, "d_model": DM, "d_inner": D, "dt_rank": R,
+                   "d_state": N, "io": w.io, "parallelism": "none (one rank's shard; its all-reduces are not built)"},
+        "layer_ms": round(total, 4), "stages": stages_rec,
+        "roofline": {"kernel": "in_proj GEMM (hipBLASLt)", "bound": "mfma", "achieved": gemm["tflops"],
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": gemm["mfma_frac"], "traffic": None},
+        "cpu_baseline": None,
+    }
+    pj.close()
+    if not args.no_cpu_baseline:
+        log("bench: timing the layer oracle on the host")
+        rec["cpu_baseline"] = layer_cpu_baseline(w, hidden, wts, prm, tokens=1024)
+    print(json.dumps(rec), flush=True)
+
+
+def layer_cpu_baseline(w, hidden, wts, prm, tokens):
+    """The oracle's layer (numpy fp64 projections, the C scan on all host cores) on the first
+    `tokens` tokens of batch row 0."""
+    import oracle
+    from oracle import proj as P
+
+    h = hidden[:1, :tokens].cpu()
+    wc = {k: v.cpu() for k, v in wts.items()}
+    pc = {k: v.cpu() for k, v in prm.items()}
+    cores = oracle.default_threads()
+    t0 = time.perf_counter()
+    P.layer_prefill(h, wc, pc, w.io, nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {tokens} tokens of the layer (batch row 0): numpy fp64 projections (one thread) and the "
+                      f"C fp64 scan over {cores} threads", "seconds": round(dt, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +401,9 @@ def main():
     ap.add_argument("--codec", metavar="AGGREGATE", default=None,
                     help="instead of the scan, time the int8 codec on an aggregation-tensor workload "
                          "(tp_prefill_7b or tp_decode_2.8b) and print its own JSON line")
+    ap.add_argument("--layer", metavar="LAYER", default=None,
+                    help="instead of the scan alone, time one rank's mixer layer (layer7b): projections, conv "
+                         "front, scan, and print its own JSON line")
     ap.add_argument("--record-traffic", metavar="PMC_DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs and exit")
     args = ap.parse_args()
@@ -304,6 +419,9 @@ def main():
 
     if args.codec:
         bench_codec(args)
+        return
+    if args.layer:
+        bench_layer(args)
         return
 
     import torch

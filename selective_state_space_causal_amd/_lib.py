@@ -358,7 +358,8 @@ class Projector:
             Bn, K2, L = x.shape
         if K2 != K:
             raise ValueError(f"in_features mismatch: input has {K2}, weight has {K}")
-        out_dtype = x.dtype if out_dtype is None else out_dtype
+        if out_dtype is None:
+            out_dtype = x.dtype if out is None else out.dtype
         shape = (Bn, M, L) if token_major_in else (Bn, L, M)
         if out is None:
             out = torch.empty(shape, dtype=out_dtype, device=x.device)
