@@ -12,7 +12,6 @@ oracle timed on this host's cores on the same input bits.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -51,9 +50,19 @@ def decode_bytes(B, D, N, es):
     return B * D * (2 * (N + CONV_W - 1) * 4 + 4 * es) + D * (N + 7) * 4 + B * 2 * N * es
 
 
-def kernel_source_hash():
+# The sources each measured kernel is built from: a traffic record stays valid while these
+# files are unchanged (a change elsewhere in the library does not touch that kernel).
+KERNEL_SOURCES = {
+    "scan": ["ssm_windowed.hip", "ssm_decode.hip", "ssm_seq.hip", "ssm_device.h", "ssm_internal.h"],
+    "codec": ["ssm_codec.hip", "ssm_device.h"],
+}
+
+
+def kernel_source_hash(group="scan"):
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_causal_amd", "csrc", "*"))):
+    for name in KERNEL_SOURCES[group]:
+        f = os.path.join(ROOT, "selective_state_space_causal_amd", "csrc", name)
+        h.update(name.encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
@@ -69,7 +78,7 @@ def traffic_from_profiles(workload, kernel=None):
         rec = json.load(open(path)).get(workload)
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(rec.get("sources", "scan")):
         return None
     if kernel is not None:
         return (rec.get(kernel) or {}).get("bytes_per_launch")
@@ -122,7 +131,8 @@ def record_traffic(pmc_dir, workload):
     rec = json.load(open(path)) if os.path.exists(path) else {}
     codec = kernel("q8_") is not None
     cmd = (PMC_COMMAND_CODEC if codec else PMC_COMMAND).format(ctr="<FETCH_SIZE|WRITE_SIZE>", workload=workload)
-    entry = {"source_hash": kernel_source_hash(), "command": cmd,
+    group = "codec" if codec else "scan"
+    entry = {"sources": group, "source_hash": kernel_source_hash(group), "command": cmd,
              "copy_calibration": {"kernel": copy_name, "fetch_scale": round(fetch_scale, 4),
                                   "write_scale": round(write_scale, 4)}}
     if codec:
