@@ -31,10 +31,12 @@
  *
  * Conventions (as in ssm.h): device pointers owned by the caller; calls are stream-ordered
  * and asynchronous; arguments are validated on the host first, and an invalid call returns a
- * non-zero ssm_status and enqueues nothing.  A projection context holds a hipBLASLt handle
- * and a cache of the algorithms chosen per shape: create one per host thread (a context is
- * not safe for concurrent use); it allocates host memory only.  Device scratch comes from the
- * caller (ssm_proj_workspace_bytes).
+ * non-zero ssm_status and enqueues nothing.  A projection context holds a hipBLASLt handle,
+ * created for the device current at ssm_proj_create and valid only on it, and a cache of the
+ * algorithm chosen per shape: create one per host thread (a context is not safe for
+ * concurrent use).  ssm_proj itself allocates no device memory: its scratch is the caller's
+ * workspace (ssm_proj_workspace_bytes); what hipBLASLt sets up inside its handle at creation
+ * is hipBLASLt's.
  */
 #ifndef SSM_PROJ_H
 #define SSM_PROJ_H
