@@ -8,7 +8,7 @@
 //   1. lane i takes tokens [t0 + i*K, t0 + (i+1)*K): loads x / dt / z with one 16-byte
 //      vector load each, runs the conv + SiLU + softplus front end in registers (the
 //      three previous raw inputs come from lane i-1 through a DPP wave shift);
-//   2. per group of states (8 for bf16 io, 4 for fp32 io), each lane reduces its K tokens
+//   2. per group of 8 or 4 states (the launch shapes below), each lane reduces its K tokens
 //      to one affine pair (P, H) = (prod a_t, state reached from zero), keeping every a_t
 //      and b_t in registers;
 //   3. a Kogge-Stone scan of the pairs across the 64 lanes with DPP (row_shr 1/2/4/8,
@@ -30,14 +30,17 @@ constexpr int NS = 16;              // d_state handled by this kernel
 constexpr int K = 8;                // tokens per lane per window
 constexpr int WAVE = 64;
 constexpr int WIN = WAVE * K;       // tokens per window
-constexpr int W = 8;                // waves (channels) per workgroup
-constexpr int THREADS = W * WAVE;
-// States per replay group: 8 independent chains per pass for bf16 io (more in flight per wave;
-// fits the 256-VGPR budget of two waves per SIMD), 4 for fp32 io, whose wider prefetch
-// registers would otherwise spill.  Per state the arithmetic is the same either way, so the
-// two choices give bit-identical results.
-template <typename IO>
-constexpr int group_states() { return sizeof(IO) == 2 ? 8 : 4; }
+// Launch shapes (waves per workgroup W = channels per workgroup, states per replay group G).
+// Per channel the arithmetic is the same in every shape -- same windows, same per-state
+// operations in the same order -- so every shape gives bit-identical results, and the choice
+// may follow the channel count:
+//   W 8,  G 8: bf16 io with few channels (two waves per SIMD: eight independent state chains
+//              per pass keep each wave busy; 248 VGPRs);
+//   W 12, G 4: bf16 io with at least 12288 channels and 16-byte aligned rows (three waves per
+//              SIMD; 168 VGPRs): 7-12% faster there (mamba2.8b, long64k), slower when there
+//              are too few workgroups;
+//   W 8,  G 4: fp32 io (its wider prefetch registers would spill with more).
+constexpr int kManyChannels = 12288;
 constexpr int LANE_STRIDE = K * NS + 4;  // floats per lane block in LDS (+4: conflict-free b128)
 
 // GFX9 DPP control: each lane reads lane - 1 of the whole wave (lane 0 has no source).
@@ -227,11 +230,11 @@ __device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, 
 // Window B / C staging: one io tensor's tile is WIN * NS values, moved as 16-byte chunks
 // (a batch row of B or C is L * 16 io values, a multiple of 16 bytes, so a chunk is either
 // wholly inside the row or wholly past its end and then reads as zeros).
-template <typename IO>
+template <typename IO, int THREADS>
 struct TileChunks {
   static constexpr int EPC = 16 / sizeof(IO);          // io elements per chunk
   static constexpr int CHUNKS = WIN * NS / EPC;        // chunks per tensor per window
-  static constexpr int PER_THREAD = CHUNKS / THREADS;
+  static constexpr int PER_THREAD = (CHUNKS + THREADS - 1) / THREADS;
   uint32_t b[PER_THREAD][4], c[PER_THREAD][4];
 
   __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rc, int soff) {
@@ -252,6 +255,7 @@ struct TileChunks {
 #pragma unroll
     for (int r = 0; r < PER_THREAD; ++r) {
       const int ci = threadIdx.x + r * THREADS;
+      if (CHUNKS % THREADS != 0 && ci >= CHUNKS) break;  // fetched (harmless) but not staged
       const int token = ci * EPC / NS;
       const int s0 = (ci * EPC) % NS;
       const int off = (token / K) * LANE_STRIDE + (token % K) * NS + s0;
@@ -273,8 +277,9 @@ struct TileChunks {
   }
 };
 
-template <typename IO, bool ALIGNED>
-__global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
+template <typename IO, bool ALIGNED, int W, int G>
+__global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
+  constexpr int THREADS = W * WAVE;
   __shared__ Tile tiles[2];  // window w reads tiles[w & 1] while window w + 1's goes into the other
   constexpr int ES = sizeof(IO);
   const int lane = threadIdx.x & (WAVE - 1);
@@ -322,7 +327,7 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
 
   const int nwin = (int)((Lb + WIN - 1) / WIN);
   const int voff = lane * K * ES;  // this lane's byte offset inside a window
-  TileChunks<IO> pf;
+  TileChunks<IO, THREADS> pf;
   Lanes<IO, ALIGNED> px, pdt, pz;
   pf.fetch(rB, rC, 0);
   px.load(rx, voff, 0);
@@ -384,7 +389,6 @@ __global__ __launch_bounds__(THREADS) void prefill_windowed(ScanArgs a) {
     // ---- state groups: local pairs, lane scan, replay ----
     const float* tb = &tile.B[lane * LANE_STRIDE];
     const float* tcp = &tile.C[lane * LANE_STRIDE];
-    constexpr int G = group_states<IO>();
 #pragma unroll
     for (int q0 = 0; q0 < NS; q0 += G) {
       float av[K][G], bv[K][G], P[G], H[G];
@@ -467,15 +471,21 @@ bool windowed_supported(const ScanArgs& a) {
   return a.N == NS && a.L * NS * es < ((int64_t)1 << 31) - WIN * NS * es;
 }
 
-hipError_t launch_windowed(const ScanArgs& a, hipStream_t s) {
+template <typename IO, int W, int G>
+void launch_shape(const ScanArgs& a, bool aligned, hipStream_t s) {
   const int64_t groups = (a.D + W - 1) / W;
-  const dim3 grid((unsigned)(a.B * groups)), block(THREADS);
+  const dim3 grid((unsigned)(a.B * groups)), block(W * WAVE);
+  if (aligned) prefill_windowed<IO, true, W, G><<<grid, block, 0, s>>>(a);
+  else prefill_windowed<IO, false, W, G><<<grid, block, 0, s>>>(a);
+}
+
+hipError_t launch_windowed(const ScanArgs& a, hipStream_t s) {
   if (a.bf16) {
-    if (a.L % 8 == 0) prefill_windowed<bf16_t, true><<<grid, block, 0, s>>>(a);
-    else prefill_windowed<bf16_t, false><<<grid, block, 0, s>>>(a);
+    const bool aligned = a.L % 8 == 0;
+    if (a.B * a.D >= kManyChannels && aligned) launch_shape<bf16_t, 12, 4>(a, true, s);
+    else launch_shape<bf16_t, 8, 8>(a, aligned, s);
   } else {
-    if (a.L % 4 == 0) prefill_windowed<float, true><<<grid, block, 0, s>>>(a);
-    else prefill_windowed<float, false><<<grid, block, 0, s>>>(a);
+    launch_shape<float, 8, 4>(a, a.L % 4 == 0, s);
   }
   return hipGetLastError();
 }

@@ -261,3 +261,21 @@ def test_bf16_output_is_rne_of_fp32_output(L, D):
     u32 = ssm.decode_step(t32["x"], t32["dt"], t32["z"], t32["Bm"], t32["Cm"], prm, h32, c32)
     assert torch.equal(u16.view(torch.int16), u32.to(torch.bfloat16).view(torch.int16))
     assert torch.equal(h16, h32) and torch.equal(c16, c32)
+
+
+def test_launch_shapes_agree_bitwise():
+    """With 12288 or more channels the bf16 prefill runs 12 channels per workgroup in groups of
+    4 states; a single batch row of the same problem has fewer channels and runs 8 per
+    workgroup in groups of 8.  Per channel the arithmetic is the same, so both must give the
+    same bits (the channel-slice invariant, across launch shapes)."""
+    B, L, D, N = 4, 1040, 3200, 16
+    note(f"launch shapes: B={B} L={L} D={D}")
+    prm = dev(I.make_params(D, N, seed=51))
+    seq = I.make_sequence_device(B, L, D, N, "bf16", seed=51, device=DEV)
+    y, h, c = ssm.prefill(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], prm)
+    for b in range(B):
+        one = {k: v[b:b + 1].contiguous() for k, v in seq.items()}
+        yb, hb, cb = ssm.prefill(one["x"], one["dt"], one["z"], one["Bm"], one["Cm"], prm)
+        torch.cuda.synchronize()
+        assert torch.equal(yb[0].view(torch.int16), y[b].view(torch.int16)), b
+        assert torch.equal(hb[0], h[b]) and torch.equal(cb[0], c[b]), b
