@@ -89,9 +89,10 @@ typedef struct {
   int32_t chunk_hint; /* prefill decomposition: 0 = automatic, 1 = one lane per channel walking
                          its tokens in order, 8 = one wave per channel with 8 tokens per lane
                          (d_state 16 only; otherwise the one-lane form runs).  Any other value
-                         is SSM_ERR_SHAPE.  The automatic choice depends on d_state and L only,
-                         never on batch or d_inner, so a channel slice run alone reproduces the
-                         full run bit for bit. */
+                         is SSM_ERR_SHAPE.  The automatic choice of decomposition depends on
+                         d_state and L only; the workgroup shape may follow batch * d_inner but
+                         never changes a result bit.  So a channel slice or a batch row run
+                         alone reproduces the full run bit for bit. */
 } ssm_dims;
 
 /* Per-channel parameters, device fp32.  conv_b may be NULL (zero bias). */
