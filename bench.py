@@ -211,10 +211,27 @@ def cpu_baseline(w, prm, seq_dev, toks_dev):
         _, h, c = oracle.decode_step(tok, prm, h, c, nthreads=cores)
     t3 = time.perf_counter()
     elems = w.batch * w.seqlen * w.d_inner
+    # one core: the same prefill on a 1/cores share of the channels (work is linear in channels)
+    sub = max(1, w.d_inner // cores)
+    seq1 = {k: (v[:, :sub].contiguous() if k in ("x", "dt", "z") else v) for k, v in seq.items()}
+    prm1 = {k: (None if v is None else v[:sub].contiguous()) for k, v in prm.items()}
+    t4 = time.perf_counter()
+    oracle.prefill(seq1, prm1, nthreads=1)
+    t5 = time.perf_counter()
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(elems / (t1 - t0) / 1e9, 4), "unit": "Gelem/s", "cores": cores, "kind": "oracle",
             "sample": f"whole prefill of the workload ({w.batch}x{w.seqlen}x{w.d_inner} elements) on the same bf16 "
                       f"bits, then {T} decode steps from the oracle's own cache; threads over channels",
-            "prefill_s": round(t1 - t0, 3), "decode_us_per_step": round((t3 - t2) / max(T, 1) * 1e6, 1)}
+            "prefill_s": round(t1 - t0, 3), "decode_us_per_step": round((t3 - t2) / max(T, 1) * 1e6, 1),
+            "value_1core": round(w.batch * w.seqlen * sub / (t5 - t4) / 1e9, 5),
+            "sample_1core": f"{sub} of the {w.d_inner} channels on one thread", "cpu_model": model}
 
 
 def codec_bytes(n, nb, es, parts):
@@ -449,7 +466,10 @@ def main():
                     "instead of replaying the captured HIP graph")
     ap.add_argument("--chunk-hint", type=int, default=0, help="prefill decomposition (0 auto, 1 sequential, 8 windowed)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+                    help="also run one plain 1 GiB device copy (for scaling rocprofv3 byte counters; the scan "
+                         "bench always times one)")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 1 GiB scrub buffer (4x the last-level cache) before each timed prefill")
     ap.add_argument("--pool", action="store_true",
                     help="serving form: ragged prompt lengths (uniform in [L/2, L]) and a cache pool of 2*batch "
                          "entries addressed through a random slot map (ssm_prefill_pool / ssm_decode_step_pool)")
@@ -504,16 +524,22 @@ def main():
     nws = ssm.workspace_bytes(B, L, D, N, seq["x"].dtype)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
 
-    if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log("bench: copy calibration: 1 GiB read + 1 GiB written")
-        del src, dst
-
     stream = torch.cuda.current_stream()
     ev = TimingEvent
+    # Context for the HBM fractions: a plain 1 GiB device copy, timed (it is also the byte-counter
+    # calibration dispatch of --copy-calibration runs).
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = ev(), ev()
+    c0.record(stream)
+    dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    log(f"bench: plain 1 GiB copy: {copy_gbps:.0f} GB/s (read + write)")
+    del src, dst
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
     elems = B * L * D
     if args.pool:
         g = torch.Generator().manual_seed(1)
@@ -553,6 +579,8 @@ def main():
 
     def step(marks):
         e0, e1, e2 = ev(), ev(), ev()
+        if scrub is not None:  # cold: 1 GiB written (4x the last-level cache) before the timed region
+            scrub.fill_(0.0)
         e0.record(stream)
         if args.pool:
             ssm.prefill_pool(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], pd, slots_d, hp, cp,
@@ -625,6 +653,9 @@ def main():
                         "frac": round(p_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": pbytes},
         "decode_hbm": None if not T else {"achieved": round(d_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                           "frac": round(d_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": dbytes},
+        "copy_gbps": round(copy_gbps, 1),
+        "cache_state": "cold (1 GiB scrub before each prefill)" if args.cold else "warm",
+        "cache_benefit": None if not T else round(pre_ms * 1e3 / d_us, 1),
         "roofline": {"kernel": "prefill", "bound": "alu", "achieved": round(tflops, 3),
                      "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
                      "flops_per_element": flops_per_element(N), "traffic": traffic},
