@@ -457,8 +457,8 @@ def layer_cpu_baseline(w, hidden, wts, prm, tokens):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="slice7b")
     ap.add_argument("--decode-steps", type=int, default=None, help="override the workload's decode step count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -553,14 +553,17 @@ def main():
         cp = torch.zeros(pool, D, CONV_W - 1, dtype=torch.float32, device=dev)
         log(f"bench: pool form: {pool} cache entries, lengths {int(lens.min())}..{int(lens.max())}")
 
+    def decode_one(t, s=None):
+        tk = toks[t]
+        if args.pool:
+            ssm.decode_step_pool(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, slots_d, hp, cp,
+                                 y_t=ys[t], stream=s)
+        else:
+            ssm.decode_step(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, h, c, y_t=ys[t], stream=s)
+
     def decode_loop(s=None):
         for t in range(T):
-            tk = toks[t]
-            if args.pool:
-                ssm.decode_step_pool(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, slots_d, hp, cp,
-                                     y_t=ys[t], stream=s)
-            else:
-                ssm.decode_step(tk["x"], tk["dt"], tk["z"], tk["Bm"], tk["Cm"], pd, h, c, y_t=ys[t], stream=s)
+            decode_one(t, s)
 
     # The decode loop as a serving loop runs it: captured once in a HIP graph, replayed per
     # request.  (An eager, one-launch-per-call loop is timed separately below.)
@@ -618,8 +621,23 @@ def main():
         torch.cuda.synchronize()
         eager_us = e0.elapsed_time(e1) * 1e3 / T
 
-    pre_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / len(marks)
-    dec_ms = sum(b.elapsed_time(c_) for _, b, c_ in marks) / len(marks)
+    cold_first_us = None
+    if T:  # one decode step with every cache scrubbed first: the first token after an idle spell
+        scrub_c = scrub if scrub is not None else torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        scrub_c.fill_(0.0)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        decode_one(0, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold_first_us = e0.elapsed_time(e1) * 1e3
+        del scrub_c
+
+    pre_each = sorted(a.elapsed_time(b) for a, b, _ in marks)
+    dec_each = sorted(b.elapsed_time(c_) for _, b, c_ in marks)
+    pre_ms = sum(pre_each) / len(pre_each)
+    dec_ms = sum(dec_each) / len(dec_each)
+    median = lambda v: 0.5 * (v[(len(v) - 1) // 2] + v[len(v) // 2])
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     gelem = elems / (pre_ms * 1e-3) / 1e9
     pbytes = prefill_bytes(B, L, D, N, es)
@@ -646,13 +664,19 @@ def main():
                    "parallelism": "none (one GPU's channel slice)",
                    "tokens": elems // D, "pool_entries": 2 * B if args.pool else None},
         "prefill_ms": round(pre_ms, 4),
+        "prefill_ms_median": round(median(pre_each), 4),
+        "prefill_ms_range": [round(pre_each[0], 4), round(pre_each[-1], 4)],
         "decode_us_per_step": None if d_us is None else round(d_us, 3),
+        "decode_us_per_step_median": None if not T else round(median(dec_each) * 1e3 / T, 3),
         "decode_mode": "hip_graph" if graph is not None else "eager",
         "decode_us_per_step_eager": None if eager_us is None else round(eager_us, 3),
+        "decode_us_cold_first_step": None if cold_first_us is None else round(cold_first_us, 3),
         "prefill_hbm": {"achieved": round(p_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(p_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": pbytes},
+                        "frac": round(p_gbps / HBM_PEAK_GBPS, 4), "frac_of_copy": round(p_gbps / copy_gbps, 4),
+                        "algorithmic_bytes": pbytes},
         "decode_hbm": None if not T else {"achieved": round(d_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                          "frac": round(d_gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": dbytes},
+                                          "frac": round(d_gbps / HBM_PEAK_GBPS, 4),
+                                          "frac_of_copy": round(d_gbps / copy_gbps, 4), "algorithmic_bytes": dbytes},
         "copy_gbps": round(copy_gbps, 1),
         "cache_state": "cold (1 GiB scrub before each prefill)" if args.cold else "warm",
         "cache_benefit": None if not T else round(pre_ms * 1e3 / d_us, 1),
