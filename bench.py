@@ -344,12 +344,13 @@ def bench_codec(args):
 
 
 def bench_layer(args):
-    """One step = one rank's mixer layer over the prompt: in_proj (x, z), conv front, x_proj
-    (low-rank step input, B, C), dt_proj, the scan, out_proj (fp32 partial)."""
+    """One step = one rank's mixer layer over the prompt: in_proj (x and z), conv front, x_proj
+    (low-rank step input, B, C), dt_proj, the scan, out_proj (partial in the io dtype)."""
     import torch
 
     import selective_state_space_causal_amd as ssm
     from selective_state_space_causal_amd import inputs as I
+    from selective_state_space_causal_amd import layer
 
     w = I.LAYERS[args.layer]
     dev = torch.device("cuda:0")
@@ -361,33 +362,15 @@ def bench_layer(args):
     wts = I.make_proj_weights(DM, D, R, N, w.io, device=dev)
     hidden = I.make_hidden(B, L, DM, w.io, device=dev)
     pj = ssm.Projector(dev)
-    dt_ = hidden.dtype
-    x = torch.empty(B, D, L, dtype=dt_, device=dev)
-    z, u, dtt = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
-    lowrank = torch.empty(B, L, R, dtype=dt_, device=dev)
-    Bm, Cm = torch.empty(B, L, N, dtype=dt_, device=dev), torch.empty(B, L, N, dtype=dt_, device=dev)
-    y = torch.empty_like(x)
-    h = torch.empty(B, D, N, dtype=torch.float32, device=dev)
-    c = torch.empty(B, D, CONV_W - 1, dtype=torch.float32, device=dev)
-    out = torch.empty(B, L, DM, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    names = ["in_proj_x", "in_proj_z", "conv_silu", "x_proj_dt", "x_proj_B", "x_proj_C", "dt_proj", "scan", "out_proj"]
-
-    def stages():
-        yield lambda: pj(ssm.PROJ_IN, hidden, wts["in_x"], out=x, stream=stream)
-        yield lambda: pj(ssm.PROJ_IN, hidden, wts["in_z"], out=z, stream=stream)
-        yield lambda: ssm.conv_silu(x, prm, u=u, stream=stream)
-        yield lambda: pj(ssm.PROJ_X, u, wts["x_dt"], out=lowrank, stream=stream)
-        yield lambda: pj(ssm.PROJ_X, u, wts["x_B"], out=Bm, stream=stream)
-        yield lambda: pj(ssm.PROJ_X, u, wts["x_C"], out=Cm, stream=stream)
-        yield lambda: pj(ssm.PROJ_DT, lowrank, wts["dt"], out=dtt, stream=stream)
-        yield lambda: ssm.prefill(x, dtt, z, Bm, Cm, prm, y=y, h_out=h, conv_out=c, stream=stream)
-        yield lambda: pj(ssm.PROJ_OUT, y, wts["out"], out=out, stream=stream)
+    bufs = layer.alloc_buffers(hidden, wts, N)
+    plan = layer.stages(hidden, wts, prm, pj, bufs, stream)
+    names = [n for n, _ in plan]
 
     def step(marks):
         evs = [TimingEvent() for _ in range(len(names) + 1)]
         evs[0].record(stream)
-        for i, f in enumerate(stages()):
+        for i, (_, f) in enumerate(plan):
             f()
             evs[i + 1].record(stream)
         marks.append(evs)
@@ -405,7 +388,8 @@ def bench_layer(args):
     ms = [sum(m[i].elapsed_time(m[i + 1]) for m in marks) / len(marks) for i in range(len(names))]
     total = sum(ms)
     tokens = B * L
-    flops = {"in_proj_x": 2 * tokens * DM * D, "in_proj_z": 2 * tokens * DM * D, "x_proj_dt": 2 * tokens * D * R,
+    flops = {"in_proj_xz": 4 * tokens * DM * D, "in_proj_x": 2 * tokens * DM * D, "in_proj_z": 2 * tokens * DM * D,
+             "x_proj_dt": 2 * tokens * D * R,
              "x_proj_B": 2 * tokens * D * N, "x_proj_C": 2 * tokens * D * N, "dt_proj": 2 * tokens * R * D,
              "out_proj": 2 * tokens * D * DM}
     stages_rec = {}
@@ -416,7 +400,7 @@ def bench_layer(args):
             e.update({"tflops": round(tf, 1), "mfma_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)})
         stages_rec[n] = e
     log("bench: " + ", ".join(f"{n} {t * 1e3:.1f} us" for n, t in zip(names, ms)) + f"; layer {total:.3f} ms")
-    gemm = stages_rec["in_proj_x"]
+    gemm = stages_rec[names[0]]
     rec = {
         "metric": "mixer layer tokens/s (one rank's channel slice: projections, conv front, scan)",
         "value": round(tokens / (total * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -85,11 +85,12 @@ def to_io(a, io: str) -> np.ndarray:
     return t.double().numpy()
 
 
-def layer_prefill(hidden, w: dict, params: dict, io: str = "bf16", nthreads: int = 1):
+def layer_prefill(hidden, w: dict, params: dict, io: str = "bf16", nthreads: int = 1, out_io: bool = True):
     """One rank's mixer layer over a prompt, as the library composes it: in_proj (x, z),
     conv front, x_proj (low-rank step input, B, C), dt_proj, the scan (the C oracle), and
-    out_proj as an fp32 partial; every intermediate tensor the GPU stores in the io dtype is
-    rounded to it here at the same point.  Returns (out [B, L, d_model] fp64, h, conv)."""
+    out_proj, whose partial is rounded to the io dtype when out_io (else kept exact); every
+    intermediate tensor the GPU stores in the io dtype is rounded to it here at the same
+    point.  Returns (out [B, L, d_model] fp64, h, conv)."""
     from . import prefill as scan_prefill  # the fp64 C oracle of the scan
 
     x = to_io(in_proj(hidden, w["in_x"]), io)
@@ -102,4 +103,5 @@ def layer_prefill(hidden, w: dict, params: dict, io: str = "bf16", nthreads: int
     y, h, c = scan_prefill({"x": x, "dt": dt, "z": z, "Bm": Bm, "Cm": Cm},
                            {k: _f64(v) for k, v in params.items() if v is not None}, nthreads=nthreads)
     y = to_io(y, io)
-    return out_proj(y, w["out"]), h, c
+    out = out_proj(y, w["out"])
+    return (to_io(out, io) if out_io else out), h, c

@@ -194,7 +194,8 @@ def make_aggregate(tokens: int, d_model: int, io: str = "bf16", seed: int = 0, p
 # Page 1 (Methodology item 1) splits the mixer's projection weights across GPUs along the
 # feature dimension.  Stand-in weights for one rank's shard, random-initialised at the usual
 # 1/sqrt(fan_in) scale (no trained weights are used):
-#   in_x, in_z [D, d_model]      N(0, 1/d_model)   column shard of the input projection
+#   in_xz [2D, d_model]          N(0, 1/d_model)   column shard of the input projection: rows
+#                                                  [0, D) make x (in_x), rows [D, 2D) make z (in_z)
 #   x_dt [R, D], x_B [N, D], x_C [N, D]  N(0, 1/D)  the rows of x_proj that read these channels
 #   dt [D, R]                    N(0, 1/R) * 0.5   step-size projection of these channels
 #   out [d_model, D]             N(0, 1/D)         row shard of the output projection
@@ -231,8 +232,11 @@ def make_proj_weights(d_model: int, d_inner: int, dt_rank: int, d_state: int, io
         g.manual_seed(torch_seed(seed, "proj", name))
         return (torch.randn(shape, generator=g, device=device) * std).to(dtype)
 
-    return {"in_x": normal("in_x", (d_inner, d_model), d_model ** -0.5),
-            "in_z": normal("in_z", (d_inner, d_model), d_model ** -0.5),
+    # in_proj's shard is one [2 d_inner, d_model] tensor (x rows, then z rows); in_x and in_z
+    # are its halves (views).
+    in_xz = torch.cat([normal("in_x", (d_inner, d_model), d_model ** -0.5),
+                       normal("in_z", (d_inner, d_model), d_model ** -0.5)])
+    return {"in_xz": in_xz, "in_x": in_xz[:d_inner], "in_z": in_xz[d_inner:],
             "x_dt": normal("x_dt", (dt_rank, d_inner), d_inner ** -0.5),
             "x_B": normal("x_B", (d_state, d_inner), d_inner ** -0.5),
             "x_C": normal("x_C", (d_state, d_inner), d_inner ** -0.5),

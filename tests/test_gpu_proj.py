@@ -104,16 +104,24 @@ def test_conv_silu_resume_is_bitwise():
         assert torch.equal(tail, full[:, :, L1:]), L1
 
 
-def test_layer_small_matches_oracle(pj):
+@pytest.mark.parametrize("rows,out_f32", [(2, False), (1, False), (2, True)])
+def test_layer_small_matches_oracle(pj, rows, out_f32):
+    """Two batch rows run in_proj as two GEMMs (x rows, z rows); one row runs it as one GEMM
+    over the stacked weight.  The out partial in bf16 (default) or fp32."""
     w8 = I.LAYERS["layer_small"]
-    note(f"layer {w8}")
+    note(f"layer {w8} rows={rows} out_f32={out_f32}")
     prm = I.make_params(w8.d_inner, w8.d_state)
     wts = I.make_proj_weights(w8.d_model, w8.d_inner, w8.dt_rank, w8.d_state, w8.io)
-    hidden = I.make_hidden(w8.batch, w8.seqlen, w8.d_model, w8.io)
-    out, h, c = layer.mixer_prefill(hidden.to(DEV), {k: v.to(DEV) for k, v in wts.items()},
-                                    {k: v.to(DEV) for k, v in prm.items() if v is not None}, pj)
+    hidden = I.make_hidden(w8.batch, w8.seqlen, w8.d_model, w8.io)[:rows].contiguous()
+    wd = {k: v.to(DEV) for k, v in wts.items() if k not in ("in_x", "in_z")}
+    wd["in_x"], wd["in_z"] = wd["in_xz"][:w8.d_inner], wd["in_xz"][w8.d_inner:]
+    hd = hidden.to(DEV)
+    assert layer._stacked_in_proj(hd, wd) == (rows == 1)
+    out, h, c = layer.mixer_prefill(hd, wd, {k: v.to(DEV) for k, v in prm.items() if v is not None}, pj,
+                                    out_dtype=torch.float32 if out_f32 else None)
     torch.cuda.synchronize()
-    ref, h_ref, c_ref = P.layer_prefill(hidden, wts, prm, w8.io, nthreads=threads())
+    assert out.dtype == (torch.float32 if out_f32 else hidden.dtype)
+    ref, h_ref, c_ref = P.layer_prefill(hidden, wts, prm, w8.io, nthreads=threads(), out_io=not out_f32)
     got = out.double().cpu().numpy()
     err = np.abs(got - ref) / (1 + np.abs(ref))
     note(f"layer: max err {err.max():.3e}")
