@@ -33,14 +33,22 @@ constexpr int WIN = WAVE * K;       // tokens per window
 // Launch shapes (waves per workgroup W = channels per workgroup, states per replay group G).
 // Per channel the arithmetic is the same in every shape -- same windows, same per-state
 // operations in the same order -- so every shape gives bit-identical results, and the choice
-// may follow the channel count:
-//   W 8,  G 8: bf16 io with few channels (two waves per SIMD: eight independent state chains
-//              per pass keep each wave busy; 248 VGPRs);
-//   W 12, G 4: bf16 io with at least 12288 channels and 16-byte aligned rows (three waves per
-//              SIMD; 168 VGPRs): 7-12% faster there (mamba2.8b, long64k), slower when there
-//              are too few workgroups;
+// may follow the channel count.  A workgroup of any shape fills one CU (registers and the
+// two LDS tiles), so a launch runs in rounds of one workgroup per CU:
+//   W 8,  G 8: two waves per SIMD, eight independent state chains per pass; 248 VGPRs;
+//   W 12, G 4: three waves per SIMD; 168 VGPRs; a round takes ~1.40x as long as W 8's for
+//              1.5x the channels;
+//   W 16, G 2: four waves per SIMD; at most 128 VGPRs; a round ~1.84x W 8's for 2x the channels;
 //   W 8,  G 4: fp32 io (its wider prefetch registers would spill with more).
-constexpr int kManyChannels = 12288;
+// The wider bf16 shapes need 16-byte aligned rows (their unaligned forms would spill).  For
+// bf16 io the launch takes the shape with the fewest round-weighted units,
+// ceil(workgroups / CUs) x round time: the wider shapes pay off when they need fewer rounds
+// (mamba130m's 6144 channels: 3 rounds of W 8 against 2 of W 12).
+struct ShapeCost {
+  int w;
+  float round_time;  // relative to W 8, G 8; measured on MI355X, bf16 io
+};
+constexpr ShapeCost kShapes[] = {{8, 1.0f}, {12, 1.40f}, {16, 1.84f}};
 constexpr int LANE_STRIDE = K * NS + 4;  // floats per lane block in LDS (+4: conflict-free b128)
 
 // GFX9 DPP control: each lane reads lane - 1 of the whole wave (lane 0 has no source).
@@ -114,7 +122,77 @@ __device__ __forceinline__ void scan4(float (&P)[4], float (&H)[4], float (&carr
   carry[2] = __int_as_float(s2);
   carry[3] = __int_as_float(s3);
 }
+
+// The same scan over two interleaved states (the 2-state groups of the 16-channel shape).
+// Each DPP source is written four instructions before it is read.
+#define SSM_SCAN2_STEP(CTRL)                                      \
+  "v_fmac_f32_dpp %[H0], %[H0], %[P0] " CTRL " bank_mask:0xf\n"   \
+  "v_fmac_f32_dpp %[H1], %[H1], %[P1] " CTRL " bank_mask:0xf\n"   \
+  "v_mul_f32_dpp %[P0], %[P0], %[P0] " CTRL " bank_mask:0xf\n"    \
+  "v_mul_f32_dpp %[P1], %[P1], %[P1] " CTRL " bank_mask:0xf\n"
+
+__device__ __forceinline__ void scan2(float (&P)[2], float (&H)[2], float (&carry)[2], float (&hin)[2]) {
+  float e0, e1;
+  int s0, s1;
+  asm volatile(
+      "s_nop 1\n"
+      SSM_SCAN2_STEP("row_shr:1 row_mask:0xf")
+      SSM_SCAN2_STEP("row_shr:2 row_mask:0xf")
+      SSM_SCAN2_STEP("row_shr:4 row_mask:0xf")
+      SSM_SCAN2_STEP("row_shr:8 row_mask:0xf")
+      SSM_SCAN2_STEP("row_bcast:15 row_mask:0xa")
+      SSM_SCAN2_STEP("row_bcast:31 row_mask:0xc")
+      "v_fma_f32 %[e0], %[P0], %[c0], %[H0]\n"
+      "v_fma_f32 %[e1], %[P1], %[c1], %[H1]\n"
+      "v_mov_b32 %[i0], %[c0]\n"
+      "v_mov_b32 %[i1], %[c1]\n"
+      "v_mov_b32_dpp %[i0], %[e0] wave_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mov_b32_dpp %[i1], %[e1] wave_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_readlane_b32 %[s0], %[e0], 63\n"
+      "v_readlane_b32 %[s1], %[e1], 63\n"
+      "s_nop 1\n"
+      : [H0] "+v"(H[0]), [H1] "+v"(H[1]), [P0] "+v"(P[0]), [P1] "+v"(P[1]), [e0] "=&v"(e0), [e1] "=&v"(e1),
+        [i0] "=&v"(hin[0]), [i1] "=&v"(hin[1]), [s0] "=&s"(s0), [s1] "=&s"(s1)
+      : [c0] "s"(carry[0]), [c1] "s"(carry[1]));
+  carry[0] = __int_as_float(s0);
+  carry[1] = __int_as_float(s1);
+}
+#undef SSM_SCAN2_STEP
 #undef SSM_SCAN_STEP
+
+// Scan G interleaved states (G = 2, or a multiple of 4).
+template <int G>
+__device__ __forceinline__ void scan_group(float (&P)[G], float (&H)[G], float (&carry)[G], float (&hin)[G]) {
+  if constexpr (G == 2) {
+    scan2(P, H, carry, hin);
+  } else {
+    static_assert(G % 4 == 0, "state groups of 2 or a multiple of 4");
+#pragma unroll
+    for (int g = 0; g < G; g += 4)
+      scan4(*reinterpret_cast<float(*)[4]>(&P[g]), *reinterpret_cast<float(*)[4]>(&H[g]),
+            *reinterpret_cast<float(*)[4]>(&carry[g]), *reinterpret_cast<float(*)[4]>(&hin[g]));
+  }
+}
+
+// G consecutive fp32 states of one token from the LDS tile (16-byte reads; 8-byte for G = 2).
+template <int G>
+__device__ __forceinline__ void tile_states(const float* p, float (&v)[G]) {
+  if constexpr (G == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; g += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(p + g);
+      v[g] = t.x;
+      v[g + 1] = t.y;
+      v[g + 2] = t.z;
+      v[g + 3] = t.w;
+    }
+  }
+}
 
 __device__ __forceinline__ float lane63(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
@@ -407,14 +485,7 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         float bq[G];
-#pragma unroll
-        for (int g = 0; g < G; g += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(tb + j * NS + q0 + g);
-          bq[g] = v.x;
-          bq[g + 1] = v.y;
-          bq[g + 2] = v.z;
-          bq[g + 3] = v.w;
-        }
+        tile_states<G>(tb + j * NS + q0, bq);
 #pragma unroll
         for (int q = 0; q < G; ++q) {
           av[j][q] = hw_exp2(dl[j] * A2[q0 + q]);
@@ -425,22 +496,13 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
       float hc[G], cg[G];
 #pragma unroll
       for (int q = 0; q < G; ++q) cg[q] = carry[q0 + q];
-#pragma unroll
-      for (int g = 0; g < G; g += 4) scan4(*reinterpret_cast<float(*)[4]>(&P[g]), *reinterpret_cast<float(*)[4]>(&H[g]),
-                                           *reinterpret_cast<float(*)[4]>(&cg[g]), *reinterpret_cast<float(*)[4]>(&hc[g]));
+      scan_group<G>(P, H, cg, hc);
 #pragma unroll
       for (int q = 0; q < G; ++q) carry[q0 + q] = cg[q];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         float cq[G];
-#pragma unroll
-        for (int g = 0; g < G; g += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(tcp + j * NS + q0 + g);
-          cq[g] = v.x;
-          cq[g + 1] = v.y;
-          cq[g + 2] = v.z;
-          cq[g + 3] = v.w;
-        }
+        tile_states<G>(tcp + j * NS + q0, cq);
 #pragma unroll
         for (int q = 0; q < G; ++q) {
           hc[q] = fmaf(av[j][q], hc[q], bv[j][q]);
@@ -478,21 +540,46 @@ bool windowed_supported(const ScanArgs& a) {
   return a.N == NS && a.L * NS * es < ((int64_t)1 << 31) - WIN * NS * es;
 }
 
-template <typename IO, int W, int G>
-void launch_shape(const ScanArgs& a, bool aligned, hipStream_t s) {
+template <typename IO, bool ALIGNED, int W, int G>
+void launch_shape(const ScanArgs& a, hipStream_t s) {
   const int64_t groups = (a.D + W - 1) / W;
   const dim3 grid((unsigned)(a.B * groups)), block(W * WAVE);
-  if (aligned) prefill_windowed<IO, true, W, G><<<grid, block, 0, s>>>(a);
-  else prefill_windowed<IO, false, W, G><<<grid, block, 0, s>>>(a);
+  prefill_windowed<IO, ALIGNED, W, G><<<grid, block, 0, s>>>(a);
+}
+
+// The bf16 workgroup width for this launch (see the shape table above).
+int bf16_width(const ScanArgs& a) {
+  if (a.L % 8 != 0) return 8;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 8;
+  int best = 8;
+  double best_cost = 0.0;
+  for (const ShapeCost& sh : kShapes) {
+    const int64_t wgs = a.B * ((a.D + sh.w - 1) / sh.w);
+    const double cost = (double)((wgs + cus - 1) / cus) * sh.round_time;
+    if (sh.w == 8 || cost < best_cost) {
+      best = sh.w;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_windowed(const ScanArgs& a, hipStream_t s) {
   if (a.bf16) {
-    const bool aligned = a.L % 8 == 0;
-    if (a.B * a.D >= kManyChannels && aligned) launch_shape<bf16_t, 12, 4>(a, true, s);
-    else launch_shape<bf16_t, 8, 8>(a, aligned, s);
+    switch (bf16_width(a)) {  // 12 and 16 only for aligned rows
+      case 16: launch_shape<bf16_t, true, 16, 2>(a, s); break;
+      case 12: launch_shape<bf16_t, true, 12, 4>(a, s); break;
+      default:
+        if (a.L % 8 == 0) launch_shape<bf16_t, true, 8, 8>(a, s);
+        else launch_shape<bf16_t, false, 8, 8>(a, s);
+    }
+  } else if (a.L % 4 == 0) {
+    launch_shape<float, true, 8, 4>(a, s);
   } else {
-    launch_shape<float, 8, 4>(a, a.L % 4 == 0, s);
+    launch_shape<float, false, 8, 4>(a, s);
   }
   return hipGetLastError();
 }

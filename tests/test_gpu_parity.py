@@ -264,18 +264,23 @@ def test_bf16_output_is_rne_of_fp32_output(L, D):
 
 
 def test_launch_shapes_agree_bitwise():
-    """With 12288 or more channels the bf16 prefill runs 12 channels per workgroup in groups of
-    4 states; a single batch row of the same problem has fewer channels and runs 8 per
-    workgroup in groups of 8.  Per channel the arithmetic is the same, so both must give the
-    same bits (the channel-slice invariant, across launch shapes)."""
-    B, L, D, N = 4, 1040, 3200, 16
+    """The bf16 prefill picks its workgroup shape (8, 12 or 16 channels, in state groups of 8,
+    4 or 2) from the number of workgroup rounds the launch needs, so the same channel runs in
+    different shapes depending on what else is in the launch.  Per channel the arithmetic is
+    the same, so every run must give the same bits (the channel-slice invariant, across launch
+    shapes).  On a 256-CU MI355X: all 4 rows of 3990 channels and one row alone run 16 channels
+    per workgroup; a 2990-channel slice runs 12; a 1995-channel slice runs 8 (each with a
+    ragged last workgroup)."""
+    B, L, D, N = 4, 1040, 3990, 16
     note(f"launch shapes: B={B} L={L} D={D}")
     prm = dev(I.make_params(D, N, seed=51))
     seq = I.make_sequence_device(B, L, D, N, "bf16", seed=51, device=DEV)
     y, h, c = ssm.prefill(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], prm)
     for b in range(B):
-        one = {k: v[b:b + 1].contiguous() for k, v in seq.items()}
-        yb, hb, cb = ssm.prefill(one["x"], one["dt"], one["z"], one["Bm"], one["Cm"], prm)
-        torch.cuda.synchronize()
-        assert torch.equal(yb[0].view(torch.int16), y[b].view(torch.int16)), b
-        assert torch.equal(hb[0], h[b]) and torch.equal(cb[0], c[b]), b
+        for n in (D, 2990, 1995):
+            one = {k: (v[b:b + 1, :n] if k in ("x", "dt", "z") else v[b:b + 1]).contiguous() for k, v in seq.items()}
+            pn = {k: (None if v is None else v[:n].contiguous()) for k, v in prm.items()}
+            yb, hb, cb = ssm.prefill(one["x"], one["dt"], one["z"], one["Bm"], one["Cm"], pn)
+            torch.cuda.synchronize()
+            assert torch.equal(yb[0].view(torch.int16), y[b, :n].view(torch.int16)), (b, n)
+            assert torch.equal(hb[0], h[b, :n]) and torch.equal(cb[0], c[b, :n]), (b, n)
