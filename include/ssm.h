@@ -50,6 +50,9 @@
  *   Aliasing   outputs may not overlap inputs or each other, except that the
  *              decode step updates h and conv in place by design.
  *   Device     kernels run on the calling thread's current HIP device.
+ *   Launches   a call may enqueue several kernel launches: a batch too large for one launch
+ *              (more than 2^31 work-items) is split into launches over consecutive batch
+ *              rows.  Channels are never split, so the results are the same bits.
  */
 #ifndef SSM_H
 #define SSM_H
@@ -64,11 +67,13 @@ extern "C" {
 #define SSM_ABI_VERSION 2
 #define SSM_MAX_STATE 16 /* largest supported d_state */
 #define SSM_CONV_WIDTH 4 /* the only supported d_conv */
+#define SSM_MAX_D_INNER (1 << 24) /* largest d_inner of one call */
 
 typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL = 1,      /* a required pointer is NULL */
-  SSM_ERR_SHAPE = 2,     /* a size is < 1, d_state > 16, d_conv != 4, or sizes overflow */
+  SSM_ERR_SHAPE = 2,     /* a size is < 1, d_inner > SSM_MAX_D_INNER, d_state > 16, d_conv != 4,
+                            or a byte count overflows int64 */
   SSM_ERR_DTYPE = 3,     /* io_dtype is not SSM_F32 or SSM_BF16 */
   SSM_ERR_ALIGN = 4,     /* a tensor base pointer breaks the alignment rule below */
   SSM_ERR_ALIAS = 5,     /* an output overlaps an input or another output */
@@ -82,7 +87,7 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 typedef struct {
   int64_t batch;    /* B >= 1 */
   int64_t seqlen;   /* L >= 1 */
-  int64_t d_inner;  /* D >= 1: channels of this GPU's slice */
+  int64_t d_inner;  /* D in [1, SSM_MAX_D_INNER]: channels of this GPU's slice */
   int64_t d_state;  /* N in [1, 16] */
   int64_t d_conv;   /* must be 4 */
   int32_t io_dtype; /* ssm_dtype of x, dt, z, Bm, Cm and y */

@@ -32,16 +32,17 @@ bool aligned16(const void* p) { return aligned(p, 16); }
 // Shape / dtype checks shared by both entry points.  L is validated only when use_L.
 int check_dims(const ssm_dims* d, bool use_L) {
   if (!d) return SSM_ERR_NULL;
-  if (d->batch < 1 || d->d_inner < 1 || d->d_state < 1 || d->d_state > SSM_MAX_STATE ||
+  if (d->batch < 1 || d->d_inner < 1 || d->d_inner > SSM_MAX_D_INNER || d->d_state < 1 || d->d_state > SSM_MAX_STATE ||
       d->d_conv != SSM_CONV_WIDTH || (use_L && d->seqlen < 1) ||
       (use_L && d->chunk_hint != 0 && d->chunk_hint != 1 && d->chunk_hint != 8))
     return SSM_ERR_SHAPE;
   if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
-  // Every byte count the kernels index must fit comfortably in int64.
+  // Every byte count the kernels index must fit in int64.  (Large batches are split into
+  // several launches over batch rows, so batch * d_inner has no bound of its own.)
   const int64_t L = use_L ? d->seqlen : 1, es = d->io_dtype == SSM_BF16 ? 2 : 4;
   int64_t bytes;
   if (!tensor_bytes(d->batch, d->d_inner, L, es, &bytes) || !tensor_bytes(d->batch, L, d->d_state, es, &bytes) ||
-      !tensor_bytes(d->batch, d->d_inner, d->d_state, 4, &bytes) || (d->batch * d->d_inner) > (int64_t)INT32_MAX * 256)
+      !tensor_bytes(d->batch, d->d_inner, d->d_state, 4, &bytes))
     return SSM_ERR_SHAPE;
   return SSM_OK;
 }
@@ -109,7 +110,8 @@ const char* ssm_status_str(int s) {
   switch (s) {
     case SSM_OK: return "ok";
     case SSM_ERR_NULL: return "a required pointer is NULL";
-    case SSM_ERR_SHAPE: return "invalid sizes (batch/seqlen/d_inner >= 1, 1 <= d_state <= 16, d_conv == 4)";
+    case SSM_ERR_SHAPE:
+      return "invalid sizes (batch/seqlen >= 1, 1 <= d_inner <= 2^24, 1 <= d_state <= 16, d_conv == 4)";
     case SSM_ERR_DTYPE: return "io_dtype must be SSM_F32 or SSM_BF16";
     case SSM_ERR_ALIGN: return "a tensor base pointer is misaligned (see the alignment rule in ssm.h)";
     case SSM_ERR_ALIAS: return "an output overlaps an input or another output";

@@ -30,6 +30,7 @@ constexpr float QMAX = 127.0f;
 // measured 3-8% faster on those and slower on quantize's input loads.
 constexpr int NT = 2;
 constexpr int64_t DEQUANT_MAX_GRID = 4096;  // 16 workgroups per CU
+constexpr int64_t QUANT_MAX_GRID = int64_t(1) << 20;  // keeps a launch within 2^28 work-items
 
 struct QuantArgs {
   const void* x;
@@ -99,10 +100,10 @@ __device__ __forceinline__ void load8(__amdgpu_buffer_rsrc_t r, int first, bool 
   }
 }
 
+// One workgroup's tile: elements [e0, e0 + EPW) (fewer at the end).
 template <typename IO, int BLOCK>
-__global__ __launch_bounds__(TPB) void q8_quantize(QuantArgs a) {
+__device__ __forceinline__ void quantize_tile(const QuantArgs& a, int64_t e0) {
   constexpr int LPB = BLOCK / EPL;
-  const int64_t e0 = (int64_t)blockIdx.x * EPW;
   const int64_t left = a.n - e0;
   const int cnt = left < EPW ? (int)left : EPW;  // elements of this workgroup
   const int first = threadIdx.x * EPL;
@@ -134,6 +135,13 @@ __global__ __launch_bounds__(TPB) void q8_quantize(QuantArgs a) {
       __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(w[k >> 2] >> (8 * (k & 3))), rq, first + k, 0, 0);
   }
   if (threadIdx.x % LPB == 0 && first < cnt) a.scales[e0 / BLOCK + threadIdx.x / LPB] = scale;
+}
+
+// One tile per workgroup; past QUANT_MAX_GRID tiles the workgroups stride over the rest.
+template <typename IO, int BLOCK>
+__global__ __launch_bounds__(TPB) void q8_quantize(QuantArgs a) {
+  for (int64_t e0 = (int64_t)blockIdx.x * EPW; e0 < a.n; e0 += (int64_t)gridDim.x * EPW)
+    quantize_tile<IO, BLOCK>(a, e0);
 }
 
 // One 2048-element tile of dequant-sum: elements [e0, e0 + 2048) of every part.
@@ -233,7 +241,8 @@ __global__ __launch_bounds__(TPB) void q8_dequant_sum(DequantArgs a) {
   return hipGetLastError();
 
 hipError_t launch_quantize(int io_dtype, int block, int64_t n, const QuantArgs& a, hipStream_t s) {
-  SSM_Q8_DISPATCH(q8_quantize, (n + EPW - 1) / EPW)
+  const int64_t tiles = (n + EPW - 1) / EPW;
+  SSM_Q8_DISPATCH(q8_quantize, tiles < QUANT_MAX_GRID ? tiles : QUANT_MAX_GRID)
 }
 
 hipError_t launch_dequant_sum(int io_dtype, int block, int64_t n, const DequantArgs& a, hipStream_t s) {

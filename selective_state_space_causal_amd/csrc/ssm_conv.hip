@@ -20,6 +20,7 @@ namespace {
 
 constexpr int EPL = 8;    // tokens per lane
 constexpr int TPB = 256;  // threads per workgroup
+constexpr int64_t kMaxGrid = int64_t(1) << 20;  // workgroups per launch at most
 
 struct ConvArgs {
   const void* x;
@@ -48,9 +49,9 @@ __device__ __forceinline__ float io_at(__amdgpu_buffer_rsrc_t r, int64_t i) {  /
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)(i * 4), 0, 0));
 }
 
+// Lane g of the flattened (row, 8-token group) space.
 template <typename IO, bool ALIGNED>
-__global__ __launch_bounds__(TPB) void conv_silu_kernel(ConvArgs a) {
-  const int64_t g = (int64_t)blockIdx.x * TPB + threadIdx.x;
+__device__ __forceinline__ void conv_lane(const ConvArgs& a, int64_t g) {
   const int64_t row = g / a.lanes_per_row;
   if (row >= a.rows) return;
   const int64_t t0 = (g - row * a.lanes_per_row) * EPL;
@@ -140,6 +141,15 @@ __global__ __launch_bounds__(TPB) void conv_silu_kernel(ConvArgs a) {
   }
 }
 
+// Grid-stride over lanes, so a launch of any size fits the capped grid (one pass whenever
+// the lanes fit in it).
+template <typename IO, bool ALIGNED>
+__global__ __launch_bounds__(TPB) void conv_silu_kernel(ConvArgs a) {
+  const int64_t lanes = a.rows * a.lanes_per_row;
+  for (int64_t g = (int64_t)blockIdx.x * TPB + threadIdx.x; g < lanes; g += (int64_t)gridDim.x * TPB)
+    conv_lane<IO, ALIGNED>(a, g);
+}
+
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -175,8 +185,8 @@ extern "C" int ssm_conv_silu(const ssm_dims* d, const ssm_params* p, const void*
   a.L = d->seqlen;
   a.D = d->d_inner;
   a.lanes_per_row = (d->seqlen + EPL - 1) / EPL;
-  const int64_t threads = rows * a.lanes_per_row;
-  const dim3 grid((unsigned)((threads + TPB - 1) / TPB)), tb(TPB);
+  const int64_t threads = rows * a.lanes_per_row, wgs = (threads + TPB - 1) / TPB;
+  const dim3 grid((unsigned)(wgs < kMaxGrid ? wgs : kMaxGrid)), tb(TPB);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = d->io_dtype == SSM_BF16;
   const bool al = d->seqlen % (bf ? 8 : 4) == 0;

@@ -147,7 +147,9 @@ hipError_t launch_sequential(const ScanArgs& a, hipStream_t s) {
 bool decode_quad_supported(const ScanArgs& a);
 hipError_t launch_decode_quad(const ScanArgs& a, hipStream_t s);
 
-hipError_t launch_decode(const ScanArgs& a, hipStream_t s) {
+// One launch of the decode step over a.B batch rows (the caller keeps it within the launch
+// size limit).
+hipError_t launch_decode_rows(const ScanArgs& a, hipStream_t s) {
   if (decode_quad_supported(a)) return launch_decode_quad(a, s);
   const dim3 grid = rows_grid(a), block(256);
   if (a.bf16) {

@@ -88,7 +88,8 @@ NULL, SHAPE, DTYPE, ALIGN, ALIAS, WS = 1, 2, 3, 4, 5, 6
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), SHAPE), (dict(seqlen=0), SHAPE), (dict(d_inner=-1), SHAPE), (dict(d_state=0), SHAPE),
     (dict(d_state=17), SHAPE), (dict(d_conv=3), SHAPE), (dict(chunk_hint=-2), SHAPE), (dict(chunk_hint=3), SHAPE),
-    (dict(batch=1 << 40, d_inner=1 << 30), SHAPE), (dict(io_dtype=7), DTYPE)])
+    (dict(batch=1 << 40, d_inner=1 << 20), SHAPE), (dict(d_inner=(1 << 24) + 1), SHAPE),
+    (dict(batch=1 << 20, seqlen=1 << 40), SHAPE), (dict(io_dtype=7), DTYPE)])
 def test_prefill_rejects_bad_dims(kw, code):
     assert prefill(dims(**kw), params()) == code
 
