@@ -138,6 +138,66 @@ PMC_COMMAND_CODEC = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} -d 
                      "--no-cpu-baseline --copy-calibration")
 
 
+SQ_COMMAND = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY "
+              "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU SQ_INSTS_VALU -d $REPO/gpurun_out/pmcsq -o {tag} "
+              "--output-format csv -- python3 $REPO/bench.py --workload {workload} --steps 2 --warmup 1 "
+              "--no-cpu-baseline --decode-steps 0")
+MI355X_SIMDS = 256 * 4
+
+
+def record_issue(csv_path, workload):
+    """Add the prefill kernel's VALU issue occupancy to profiles/traffic.json, from one
+    rocprofv3 --pmc run holding SQ_WAVES, SQ_WAVE_CYCLES and SQ_ACTIVE_INST_VALU (4-cycle units,
+    summed over waves): the share of each SIMD's issue slots, over the kernel's duration, in
+    which one of its waves issued a VALU instruction (a transcendental holds two slots).  The
+    kernel's duration is taken as a wave's lifetime, which holds when every wave is resident
+    from start to end (one round, as for slice7b's 2048 waves on 1024 SIMDs)."""
+    import csv
+    from collections import defaultdict
+
+    per = defaultdict(lambda: defaultdict(float))
+    name = None
+    for r in csv.DictReader(open(csv_path)):
+        if "prefill_" not in r["Kernel_Name"]:
+            continue
+        name = r["Kernel_Name"]
+        per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no prefill dispatch in {csv_path}")
+    mean = lambda k: sum(d[k] for d in per.values()) / len(per)
+    waves, cycles, active = mean("SQ_WAVES"), mean("SQ_WAVE_CYCLES"), mean("SQ_ACTIVE_INST_VALU")
+    if waves > MI355X_SIMDS * 2:
+        raise SystemExit("more than two waves per SIMD: waves are not all resident at once")
+    issue = {"kernel": name, "dispatches": len(per), "source_hash": kernel_source_hash("scan"),
+             "command": SQ_COMMAND.format(tag=os.path.basename(csv_path).split("_counter")[0], workload=workload),
+             "waves": int(waves), "wave_cycles_per_wave": round(cycles / waves, 1),
+             "active_inst_valu_per_wave": round(active / waves, 1),
+             "insts_valu_per_wave": round(mean("SQ_INSTS_VALU") / waves, 1),
+             "valu_issue_busy": round(active / (MI355X_SIMDS * cycles / waves), 4)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    rec.setdefault(workload, {})["issue"] = issue
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(issue, indent=1))
+
+
+def issue_from_profiles(workload):
+    """The prefill kernel's recorded VALU issue occupancy, or None (no record, or the kernel
+    sources changed since it was taken)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = (json.load(open(path)).get(workload) or {}).get("issue")
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash("scan"):
+        return None
+    return rec.get("valu_issue_busy")
+
+
 def record_traffic(pmc_dir, workload):
     """Turn the two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into
     profiles/traffic.json.  Each counter is scaled by what it reads for the plain 1 GiB copy
@@ -186,6 +246,8 @@ def record_traffic(pmc_dir, workload):
     else:
         entry.update({"prefill": kernel("prefill_"), "decode": kernel("decode_")})
         entry["bytes_per_launch"] = entry["prefill"]["bytes_per_launch"] if entry["prefill"] else None
+    if (rec.get(workload) or {}).get("issue"):
+        entry["issue"] = rec[workload]["issue"]  # kept: recorded from its own counter run
     rec[workload] = entry
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -465,9 +527,15 @@ def main():
                          "front, scan, and print its own JSON line")
     ap.add_argument("--record-traffic", metavar="PMC_DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs and exit")
+    ap.add_argument("--record-issue", metavar="CSV", default=None,
+                    help="add the prefill kernel's VALU issue occupancy to profiles/traffic.json from a rocprofv3 "
+                         "--pmc counter_collection.csv with SQ_WAVES, SQ_WAVE_CYCLES, SQ_ACTIVE_INST_VALU, and exit")
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(args.record_traffic, args.codec or args.workload)
+        return
+    if args.record_issue:
+        record_issue(args.record_issue, args.workload)
         return
 
     if args.gpus != 1:
@@ -666,7 +734,8 @@ def main():
         "cache_benefit": None if not T else round(pre_ms * 1e3 / d_us, 1),
         "roofline": {"kernel": "prefill", "bound": "alu", "achieved": round(tflops, 3),
                      "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
-                     "flops_per_element": flops_per_element(N), "traffic": traffic},
+                     "flops_per_element": flops_per_element(N), "traffic": traffic,
+                     "valu_issue_busy": issue_from_profiles(w.name)},
     }
     if args.pool and not args.no_cpu_baseline:
         log("bench: the CPU baseline is defined on the full workload; skipped in the pool form")
