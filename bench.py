@@ -451,7 +451,7 @@ def bench_layer(args):
     total = sum(ms)
     tokens = B * L
     flops = {"in_proj_xz": 4 * tokens * DM * D, "in_proj_x": 2 * tokens * DM * D, "in_proj_z": 2 * tokens * DM * D,
-             "x_proj_dt": 2 * tokens * D * R,
+             "x_proj_dt": 2 * tokens * D * R, "conv_xproj": 2 * tokens * D * (R + 2 * N),
              "x_proj_B": 2 * tokens * D * N, "x_proj_C": 2 * tokens * D * N, "dt_proj": 2 * tokens * R * D,
              "out_proj": 2 * tokens * D * DM}
     stages_rec = {}

@@ -87,6 +87,24 @@ int ssm_proj(ssm_proj_ctx* ctx, int32_t kind, int64_t batch, int64_t seqlen, int
 int ssm_conv_silu(const ssm_dims* dims, const ssm_params* params, const void* x, const float* conv0, void* u,
                   void* stream);
 
+/*
+ * Conv front fused into x_proj: lowrank / Bm / Cm = x_proj(u) with u = silu(conv(x)) as in
+ * ssm_conv_silu (same arithmetic, same bf16 rounding), computed on the fly and never stored.
+ *   out[b, t, m] = sum_c w[m, c] * u[b, c, t],   m < rank + 2 * d_state,
+ * rows m in [0, rank) -> lowrank [B, L, rank], [rank, rank + N) -> Bm [B, L, N], the last N ->
+ * Cm [B, L, N]: the stacked rows of x_proj that read this slice's channels (w [rank + 2N, D],
+ * row-major).  bf16 io only (SSM_ERR_DTYPE otherwise); the sums are fp32 (matrix cores) and
+ * rounded to bf16 (nearest even) once.  Uses dims (batch, seqlen, d_inner, d_state, d_conv = 4,
+ * io_dtype), params->conv_w / conv_b, conv0 as in ssm_conv_silu.
+ * Sizes: d_inner and seqlen multiples of 8 (SSM_ERR_SHAPE otherwise), rank >= 1.
+ * Alignment: x and w 16-byte, conv_w 16-byte, conv_b and conv0 4-byte, outputs 2-byte.
+ * Outputs may not overlap the inputs or each other.
+ * Passage: Methodology item 1 of the page cited above (the local mixing kernels and the
+ * projection weights of one GPU's feature slice).
+ */
+int ssm_conv_xproj(const ssm_dims* dims, const ssm_params* params, const void* x, const float* conv0, const void* w,
+                   int64_t rank, void* lowrank, void* Bm, void* Cm, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

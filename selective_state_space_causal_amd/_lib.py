@@ -86,6 +86,9 @@ def load(path: str = LIB_PATH):
                              sz, vp]
     lib.ssm_conv_silu.restype = ctypes.c_int
     lib.ssm_conv_silu.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params), vp, vp, vp, vp]
+    lib.ssm_conv_xproj.restype = ctypes.c_int
+    lib.ssm_conv_xproj.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params), vp, vp, vp, ctypes.c_int64,
+                                   vp, vp, vp, vp]
     if lib.ssm_abi_version() != ABI_VERSION:
         raise ImportError(f"libssm ABI {lib.ssm_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -388,3 +391,31 @@ def conv_silu(x, params: dict, conv0=None, *, u=None, stream=None):
     if st != 0:
         raise SsmError("ssm_conv_silu", st, lib.ssm_status_str(st).decode())
     return u
+
+
+def conv_xproj(x, params: dict, w, rank: int, conv0=None, *, lowrank=None, Bm=None, Cm=None, stream=None):
+    """The conv front fused into x_proj: for x [B, D, L] bf16 and the stacked x_proj rows
+    w [rank + 2 N, D], returns (lowrank [B, L, rank], Bm [B, L, N], Cm [B, L, N]) of
+    x_proj(silu(conv(x)))."""
+    lib = load()
+    Bn, D, L = x.shape
+    M = w.shape[0]
+    N = (M - rank) // 2
+    if w.dim() != 2 or w.shape[1] != D or rank < 1 or N < 1 or rank + 2 * N != M:
+        raise ValueError(f"w must be [rank + 2 N, {D}] with rank={rank}; got {tuple(w.shape)}")
+    _check(w, "w", (M, D), x.dtype, x.device)
+    _check(conv0, "conv0", (Bn, D, CONV_W - 1), torch.float32, x.device, optional=True)
+    outs = []
+    for t, name, width in ((lowrank, "lowrank", rank), (Bm, "Bm", N), (Cm, "Cm", N)):
+        if t is None:
+            t = torch.empty(Bn, L, width, dtype=x.dtype, device=x.device)
+        _check(t, name, (Bn, L, width), x.dtype, x.device)
+        outs.append(t)
+    d = Dims(Bn, L, D, N, CONV_W, _io_code(x.dtype), 0)
+    p = Params(None, None, None, params["conv_w"].data_ptr(),
+               None if params.get("conv_b") is None else params["conv_b"].data_ptr())
+    st = lib.ssm_conv_xproj(ctypes.byref(d), ctypes.byref(p), _ptr(x), _ptr(conv0), _ptr(w), rank,
+                            _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), stream_handle(stream))
+    if st != 0:
+        raise SsmError("ssm_conv_xproj", st, lib.ssm_status_str(st).decode())
+    return tuple(outs)

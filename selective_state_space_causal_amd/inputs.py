@@ -196,7 +196,8 @@ def make_aggregate(tokens: int, d_model: int, io: str = "bf16", seed: int = 0, p
 # 1/sqrt(fan_in) scale (no trained weights are used):
 #   in_xz [2D, d_model]          N(0, 1/d_model)   column shard of the input projection: rows
 #                                                  [0, D) make x (in_x), rows [D, 2D) make z (in_z)
-#   x_dt [R, D], x_B [N, D], x_C [N, D]  N(0, 1/D)  the rows of x_proj that read these channels
+#   x_all [R + 2N, D]            N(0, 1/D)         the rows of x_proj that read these channels:
+#                                                  x_dt [R, D], then x_B [N, D], then x_C [N, D]
 #   dt [D, R]                    N(0, 1/R) * 0.5   step-size projection of these channels
 #   out [d_model, D]             N(0, 1/D)         row shard of the output projection
 # and the layer input hidden [B, L, d_model] ~ N(0, 1).  io tensors are rounded to bf16 (RNE).
@@ -236,10 +237,13 @@ def make_proj_weights(d_model: int, d_inner: int, dt_rank: int, d_state: int, io
     # are its halves (views).
     in_xz = torch.cat([normal("in_x", (d_inner, d_model), d_model ** -0.5),
                        normal("in_z", (d_inner, d_model), d_model ** -0.5)])
+    # x_proj's rows that read these channels, stacked likewise: low-rank, then B, then C.
+    x_all = torch.cat([normal("x_dt", (dt_rank, d_inner), d_inner ** -0.5),
+                       normal("x_B", (d_state, d_inner), d_inner ** -0.5),
+                       normal("x_C", (d_state, d_inner), d_inner ** -0.5)])
     return {"in_xz": in_xz, "in_x": in_xz[:d_inner], "in_z": in_xz[d_inner:],
-            "x_dt": normal("x_dt", (dt_rank, d_inner), d_inner ** -0.5),
-            "x_B": normal("x_B", (d_state, d_inner), d_inner ** -0.5),
-            "x_C": normal("x_C", (d_state, d_inner), d_inner ** -0.5),
+            "x_all": x_all, "x_dt": x_all[:dt_rank], "x_B": x_all[dt_rank:dt_rank + d_state],
+            "x_C": x_all[dt_rank + d_state:],
             "dt": normal("dt", (d_inner, dt_rank), 0.5 * dt_rank ** -0.5),
             "out": normal("out", (d_model, d_inner), d_inner ** -0.5)}
 

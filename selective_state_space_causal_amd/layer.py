@@ -17,8 +17,11 @@ partials are used as they are.
 in_proj's shard is one [2D, d_model] weight whose first D rows make x and last D rows make z
 (the mixer's packed input projection).  With one batch row, one GEMM writes [1, 2D, L] and x
 and z are its two halves, each already a contiguous [1, D, L] tensor; otherwise the two halves
-of the weight run as two GEMMs.  out is written in the io dtype by default (the partial that
-the 8-bit all-reduce codec then quantizes); out_dtype=torch.float32 keeps it in fp32.
+of the weight run as two GEMMs.  x_proj's rows are stacked likewise ([R + 2N, D]: low-rank, B,
+C); for bf16 with D and L multiples of 8, the conv front and x_proj run as one fused kernel
+(ssm_conv_xproj) and u is never stored; otherwise u is materialised and x_proj runs as three
+GEMMs.  out is written in the io dtype by default (the partial that the 8-bit all-reduce codec
+then quantizes); out_dtype=torch.float32 keeps it in fp32.
 """
 from __future__ import annotations
 
@@ -38,6 +41,13 @@ def _stacked_in_proj(hidden, weights) -> bool:
     return (D * L * hidden.element_size()) % 16 == 0
 
 
+def _fused_conv_xproj(hidden, weights) -> bool:
+    """True when the conv front and x_proj can run as one kernel: the stacked x_proj weight,
+    bf16, and d_inner and seqlen multiples of 8."""
+    D, L = weights["in_x"].shape[0], hidden.shape[1]
+    return "x_all" in weights and hidden.dtype == torch.bfloat16 and D % 8 == 0 and L % 8 == 0
+
+
 def alloc_buffers(hidden, weights: dict, d_state: int, out_dtype=None) -> dict:
     """Every tensor the layer writes, on hidden's device."""
     B, L, DM = hidden.shape
@@ -51,7 +61,7 @@ def alloc_buffers(hidden, weights: dict, d_state: int, out_dtype=None) -> dict:
     else:
         bufs["x"] = torch.empty(B, D, L, dtype=dt, device=dev)
         bufs["z"] = torch.empty_like(bufs["x"])
-    for k in ("u", "dt", "y"):
+    for k in ("dt", "y") if _fused_conv_xproj(hidden, weights) else ("u", "dt", "y"):
         bufs[k] = torch.empty(B, D, L, dtype=dt, device=dev)
     bufs["lowrank"] = torch.empty(B, L, R, dtype=dt, device=dev)
     bufs["Bm"] = torch.empty(B, L, d_state, dtype=dt, device=dev)
@@ -71,11 +81,16 @@ def stages(hidden, weights: dict, params: dict, proj: "_lib.Projector", bufs: di
     else:
         st = [("in_proj_x", lambda: P(_lib.PROJ_IN, hidden, weights["in_x"], out=b["x"], stream=stream)),
               ("in_proj_z", lambda: P(_lib.PROJ_IN, hidden, weights["in_z"], out=b["z"], stream=stream))]
+    if "u" not in b:
+        R = weights["x_dt"].shape[0]
+        st.append(("conv_xproj", lambda: _lib.conv_xproj(b["x"], params, weights["x_all"], R, lowrank=b["lowrank"],
+                                                         Bm=b["Bm"], Cm=b["Cm"], stream=stream)))
+    else:
+        st += [("conv_silu", lambda: _lib.conv_silu(b["x"], params, u=b["u"], stream=stream)),
+               ("x_proj_dt", lambda: P(_lib.PROJ_X, b["u"], weights["x_dt"], out=b["lowrank"], stream=stream)),
+               ("x_proj_B", lambda: P(_lib.PROJ_X, b["u"], weights["x_B"], out=b["Bm"], stream=stream)),
+               ("x_proj_C", lambda: P(_lib.PROJ_X, b["u"], weights["x_C"], out=b["Cm"], stream=stream))]
     return st + [
-        ("conv_silu", lambda: _lib.conv_silu(b["x"], params, u=b["u"], stream=stream)),
-        ("x_proj_dt", lambda: P(_lib.PROJ_X, b["u"], weights["x_dt"], out=b["lowrank"], stream=stream)),
-        ("x_proj_B", lambda: P(_lib.PROJ_X, b["u"], weights["x_B"], out=b["Bm"], stream=stream)),
-        ("x_proj_C", lambda: P(_lib.PROJ_X, b["u"], weights["x_C"], out=b["Cm"], stream=stream)),
         ("dt_proj", lambda: P(_lib.PROJ_DT, b["lowrank"], weights["dt"], out=b["dt"], stream=stream)),
         ("scan", lambda: _lib.prefill(b["x"], b["dt"], b["z"], b["Bm"], b["Cm"], params, y=b["y"], h_out=b["h"],
                                       conv_out=b["c"], stream=stream)),

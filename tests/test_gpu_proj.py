@@ -104,10 +104,12 @@ def test_conv_silu_resume_is_bitwise():
         assert torch.equal(tail, full[:, :, L1:]), L1
 
 
-@pytest.mark.parametrize("rows,out_f32", [(2, False), (1, False), (2, True)])
-def test_layer_small_matches_oracle(pj, rows, out_f32):
+@pytest.mark.parametrize("rows,out_f32,fused", [(2, False, True), (1, False, True), (2, True, True),
+                                                (2, False, False)])
+def test_layer_small_matches_oracle(pj, rows, out_f32, fused):
     """Two batch rows run in_proj as two GEMMs (x rows, z rows); one row runs it as one GEMM
-    over the stacked weight.  The out partial in bf16 (default) or fp32."""
+    over the stacked weight.  The conv front and x_proj fused (the stacked x_proj weight) or
+    as conv_silu then three GEMMs.  The out partial in bf16 (default) or fp32."""
     w8 = I.LAYERS["layer_small"]
     note(f"layer {w8} rows={rows} out_f32={out_f32}")
     prm = I.make_params(w8.d_inner, w8.d_state)
@@ -115,8 +117,11 @@ def test_layer_small_matches_oracle(pj, rows, out_f32):
     hidden = I.make_hidden(w8.batch, w8.seqlen, w8.d_model, w8.io)[:rows].contiguous()
     wd = {k: v.to(DEV) for k, v in wts.items() if k not in ("in_x", "in_z")}
     wd["in_x"], wd["in_z"] = wd["in_xz"][:w8.d_inner], wd["in_xz"][w8.d_inner:]
+    if not fused:
+        del wd["x_all"]
     hd = hidden.to(DEV)
     assert layer._stacked_in_proj(hd, wd) == (rows == 1)
+    assert layer._fused_conv_xproj(hd, wd) == fused
     out, h, c = layer.mixer_prefill(hd, wd, {k: v.to(DEV) for k, v in prm.items() if v is not None}, pj,
                                     out_dtype=torch.float32 if out_f32 else None)
     torch.cuda.synchronize()
@@ -149,3 +154,77 @@ def test_in_proj_full_size_sampled(pj):
     b = w8.d_model * U * mag
     b = b + 2.0 ** -8 * (np.abs(ref) + b)
     assert np.all(np.abs(got - ref) <= b)
+
+
+def conv_magnitude(x, conv_w, conv_b, conv0):
+    """|conv_b| + sum_k |conv_w[k]| |xi[t - 3 + k]|: the scale of the conv sum's fp32 rounding."""
+    xa = np.abs(x.double().numpy())
+    B, D, Ls = xa.shape
+    hist = np.zeros((B, D, 3)) if conv0 is None else np.abs(conv0)
+    xi = np.concatenate([hist, xa], axis=2)
+    wa = np.abs(conv_w.double().numpy())
+    m = np.broadcast_to(np.abs(conv_b.double().numpy())[None, :, None], (B, D, Ls)).copy()
+    for k in range(4):
+        m += wa[None, :, k, None] * xi[:, :, k:k + Ls]
+    return m
+
+
+def bf16_flip_ulps(u64, scale):
+    """For fp64 values u64 that the GPU computes in fp32 (error within 2^-18 |u| + 2^-20 scale)
+    and then rounds to bf16: the bf16 ulp where that rounding could go either way (the value is
+    that close to a midpoint between two bf16 numbers), else 0."""
+    a = np.abs(u64)
+    nz = a > 1e-30
+    e = np.floor(np.log2(np.where(nz, a, 1.0)))
+    ulp = np.exp2(e - 7)
+    f = a / ulp
+    dist = np.abs(f - np.floor(f) - 0.5) * ulp
+    delta = 2.0 ** -18 * a + 2.0 ** -20 * scale
+    return np.where(nz & (dist <= delta), ulp, 0.0)
+
+
+@pytest.mark.parametrize("B,Ls,D,R,N,resume", [(1, 256, 64, 8, 16, False), (2, 200, 96, 256, 16, True),
+                                                (1, 136, 40, 300, 16, False), (3, 64, 2048, 48, 16, True),
+                                                (1, 8, 8, 1, 1, False), (2, 520, 136, 160, 16, False)])
+def test_conv_xproj_matches_oracle(B, Ls, D, R, N, resume):
+    """The conv front fused into x_proj against the oracle's conv front, rounded to bf16, then its
+    x_proj.  Bound per output: fp32 accumulation (D 2^-24 sum |W u|), the u elements whose bf16
+    rounding the fp32 front end may take the other way (one ulp each, found from the fp64
+    values), and the final bf16 rounding."""
+    note(f"conv_xproj B={B} L={Ls} D={D} R={R} N={N} resume={resume}")
+    prm = I.make_params(D, 16, seed=D + R)
+    prm["conv_b"] = prm["conv_b"] + 0.05
+    g = torch.Generator().manual_seed(B * 1000 + Ls + D + R)
+    x = torch.randn(B, D, Ls, generator=g).to(torch.bfloat16)
+    w = (torch.randn(R + 2 * N, D, generator=g) / D ** 0.5).to(torch.bfloat16)
+    conv0 = torch.randn(B, D, 3, generator=g).to(torch.bfloat16).float() if resume else None
+    pd = {k: v.to(DEV) for k, v in prm.items() if v is not None}
+    lr, Bm, Cm = L.conv_xproj(x.to(DEV), pd, w.to(DEV), R, None if conv0 is None else conv0.to(DEV))
+    torch.cuda.synchronize()
+    c0 = None if conv0 is None else conv0.double().numpy()
+    u64 = P.conv_silu(x, prm["conv_w"], prm["conv_b"], c0)
+    scale = conv_magnitude(x, prm["conv_w"], prm["conv_b"], c0)
+    ub = P.to_io(u64, "bf16")
+    ref = P.x_proj(ub, w)
+    mag = P.x_proj(np.abs(ub), np.abs(w.double().numpy()))
+    flips = P.x_proj(bf16_flip_ulps(u64, scale), np.abs(w.double().numpy()))
+    b = D * U * mag + flips
+    b = b + 2.0 ** -8 * (np.abs(ref) + b)
+    got = torch.cat([lr, Bm, Cm], dim=2).double().cpu().numpy()
+    err = np.abs(got - ref)
+    i = np.unravel_index(int(np.argmax(err - b)), err.shape)
+    assert np.all(err <= b), f"{i}: gpu {got[i]!r} ref {ref[i]!r} bound {b[i]:.3e}"
+    note(f"conv_xproj: u elements with an open rounding: {int((bf16_flip_ulps(u64, scale) > 0).sum())} "
+         f"of {u64.size}")
+
+
+def test_conv_xproj_errors():
+    x = torch.randn(1, 16, 64, device=DEV).to(torch.bfloat16)
+    prm = {k: v.to(DEV) for k, v in I.make_params(16, 16).items() if v is not None}
+    w = torch.randn(40, 16, device=DEV).to(torch.bfloat16)
+    with pytest.raises(L.SsmError) as e:
+        L.conv_xproj(x.float(), prm, w.float(), 8)       # fp32 io: the fused form is bf16 only
+    assert e.value.status == 3
+    with pytest.raises(L.SsmError) as e:
+        L.conv_xproj(x[:, :, :60].contiguous(), prm, w, 8)   # L not a multiple of 8
+    assert e.value.status == 2

@@ -25,7 +25,8 @@ def fake(i, off=0):
 def test_exports_every_declared_symbol():
     src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", src)))
-    assert names == ["ssm_conv_silu", "ssm_proj", "ssm_proj_create", "ssm_proj_destroy", "ssm_proj_workspace_bytes"]
+    assert names == ["ssm_conv_silu", "ssm_conv_xproj", "ssm_proj", "ssm_proj_create", "ssm_proj_destroy",
+                     "ssm_proj_workspace_bytes"]
     lib = L.load()
     for n in names:
         assert hasattr(lib, n)
@@ -79,3 +80,31 @@ def test_conv_validation():
     assert conv(cw=BASE + 5 * STEP + 8) == ALIGN and conv(cb=BASE + 6 * STEP + 2) == ALIGN
     assert conv(c0=fake(7, 1)) == ALIGN
     assert conv(u=fake(0, 64)) == ALIAS
+
+
+def xproj(B=2, Ls=64, D=16, N=16, R=8, io=L.SSM_BF16, dconv=4, x=None, w=None, o0=None, o1=None, o2=None,
+          cw=None, c0=None, dims_none=False):
+    lib = L.load()
+    d = L.Dims(B, Ls, D, N, dconv, io, 0)
+    p = L.Params(None, None, None, (BASE + 5 * STEP) if cw is None else cw, None)
+    x = fake(0) if x is None else x
+    w = fake(1) if w is None else w
+    o0 = fake(2) if o0 is None else o0
+    o1 = fake(3) if o1 is None else o1
+    o2 = fake(4) if o2 is None else o2
+    return lib.ssm_conv_xproj(None if dims_none else ctypes.byref(d), ctypes.byref(p), x, c0, w, R, o0, o1, o2, None)
+
+
+def test_conv_xproj_validation():
+    n = ctypes.c_void_p(None)
+    assert xproj(dims_none=True) == NULL and xproj(x=n) == NULL and xproj(w=n) == NULL and xproj(cw=0) == NULL
+    assert xproj(o0=n) == NULL and xproj(o1=n) == NULL and xproj(o2=n) == NULL
+    assert xproj(B=0) == SHAPE and xproj(Ls=0) == SHAPE and xproj(D=0) == SHAPE and xproj(R=0) == SHAPE
+    assert xproj(N=0) == SHAPE and xproj(N=17) == SHAPE and xproj(dconv=3) == SHAPE
+    assert xproj(D=12) == SHAPE and xproj(Ls=60) == SHAPE   # d_inner and seqlen multiples of 8
+    assert xproj(B=1 << 40, Ls=1 << 24) == SHAPE           # byte counts overflow
+    assert xproj(io=L.SSM_F32) == DTYPE and xproj(io=7) == DTYPE
+    assert xproj(x=fake(0, 8)) == ALIGN and xproj(w=fake(1, 4)) == ALIGN and xproj(o1=fake(3, 1)) == ALIGN
+    assert xproj(cw=BASE + 5 * STEP + 8) == ALIGN and xproj(c0=fake(7, 2)) == ALIGN
+    assert xproj(o0=fake(0, 64)) == ALIAS                  # lowrank inside x
+    assert xproj(o2=fake(3, 2)) == ALIAS                   # Cm overlapping Bm
