@@ -228,3 +228,34 @@ def test_conv_xproj_errors():
     with pytest.raises(L.SsmError) as e:
         L.conv_xproj(x[:, :, :60].contiguous(), prm, w, 8)   # L not a multiple of 8
     assert e.value.status == 2
+
+
+def test_conv_xproj_full_size_sampled():
+    """The fused conv front + x_proj at the 7B-class layer's size (x [1, 2048, 32768], 288 rows):
+    sampled outputs against the oracle's conv front (over the 4 raw inputs each needs) and fp64
+    dot products, with the bound of test_conv_xproj_matches_oracle."""
+    w8 = I.LAYERS["layer7b"]
+    D, Ls, R, N = w8.d_inner, w8.seqlen, w8.dt_rank, w8.d_state
+    prm = I.make_params(D, N)
+    pd = {k: v.to(DEV) for k, v in prm.items() if v is not None}
+    wall = I.make_proj_weights(w8.d_model, D, R, N, w8.io, device=DEV)["x_all"]
+    x = I.make_sequence_device(1, Ls, D, 1, "bf16", device=DEV)["x"]
+    lr, Bm, Cm = L.conv_xproj(x, pd, wall, R)
+    torch.cuda.synchronize()
+    got_all = torch.cat([lr, Bm, Cm], dim=2)[0]                       # [L, 288]
+    g = np.random.default_rng(1)
+    ts = sorted(set(int(t) for t in g.integers(0, Ls, 24)) | {0, 1, 2, 3, Ls - 1})
+    wn = wall.double().cpu().numpy()
+    for t in ts:
+        lo = max(0, t - 3)
+        xs = x[:, :, lo:t + 1].cpu()                                   # [1, D, <= 4]
+        u64 = P.conv_silu(xs, prm["conv_w"], prm["conv_b"])[0, :, -1]   # zero history before token 0
+        scale = conv_magnitude(xs, prm["conv_w"], prm["conv_b"], None)[0, :, -1]
+        ub = P.to_io(u64, "bf16")
+        ref = wn @ ub
+        mag = np.abs(wn) @ np.abs(ub)
+        flips = np.abs(wn) @ bf16_flip_ulps(u64, scale)
+        b = D * U * mag + flips
+        b = b + 2.0 ** -8 * (np.abs(ref) + b)
+        got = got_all[t].double().cpu().numpy()
+        assert np.all(np.abs(got - ref) <= b), (t, float(np.max(np.abs(got - ref) - b)))
