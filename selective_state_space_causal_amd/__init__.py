@@ -4,8 +4,8 @@
 HIP kernels for gfx950) through a thin ctypes binding; ``q8_quantize`` and
 ``q8_dequant_sum`` call the block int8 codec of include/ssm_codec.h; ``Projector``,
 ``conv_silu`` and ``conv_xproj`` call the channel-sliced projections, the conv front and the two
-fused, of include/ssm_proj.h; ``inputs`` makes seeded synthetic workloads.  Importing the package does not load the library; the first call does, and
-raises if it is not built.
+fused, of include/ssm_proj.h; ``inputs`` makes seeded synthetic workloads.  Importing the
+package does not load the library; the first call does, and raises if it is not built.
 """
 from ._lib import (PROJ_DT, PROJ_IN, PROJ_OUT, PROJ_X, Projector, SsmError, conv_silu, conv_xproj,  # noqa: F401
                    decode_step, decode_step_pool, load, prefill, prefill_pool, q8_dequant_sum, q8_num_blocks,

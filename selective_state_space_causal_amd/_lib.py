@@ -135,8 +135,10 @@ def _check_params(params: dict, D: int, N: int, device):
     _check(params.get("conv_b"), "conv_b", (D,), f32, device, optional=True)
 
 
-def stream_handle(stream=None) -> ctypes.c_void_p:
-    s = stream if stream is not None else torch.cuda.current_stream()
+def stream_handle(stream=None, device=None) -> ctypes.c_void_p:
+    """The HIP stream to enqueue on: `stream`, else the current stream of `device` (the
+    tensors' device), so kernels run where the tensors live."""
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -163,6 +165,9 @@ def prefill(x, dt, z, Bm, Cm, params: dict, h0=None, conv0=None, *, chunk_hint: 
     y = torch.empty_like(x) if y is None else y
     h_out = torch.empty(Bsz, D, N, dtype=torch.float32, device=dev) if h_out is None else h_out
     conv_out = torch.empty(Bsz, D, CONV_W - 1, dtype=torch.float32, device=dev) if conv_out is None else conv_out
+    _check(y, "y", (Bsz, D, L), io, dev)   # given outputs are written in full: their sizes must match
+    _check(h_out, "h_out", (Bsz, D, N), torch.float32, dev)
+    _check(conv_out, "conv_out", (Bsz, D, CONV_W - 1), torch.float32, dev)
     d = Dims(Bsz, L, D, N, CONV_W, _io_code(io), chunk_hint)
     need = int(lib.ssm_prefill_workspace_bytes(ctypes.byref(d)))
     if need and workspace is None:
@@ -171,7 +176,7 @@ def prefill(x, dt, z, Bm, Cm, params: dict, h0=None, conv0=None, *, chunk_hint: 
     p = make_params(params)
     st = lib.ssm_prefill(ctypes.byref(d), ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(z), _ptr(Bm), _ptr(Cm),
                          _ptr(h0), _ptr(conv0), _ptr(y), _ptr(h_out), _ptr(conv_out), _ptr(workspace),
-                         ws_bytes, stream_handle(stream))
+                         ws_bytes, stream_handle(stream, dev))
     if st != 0:
         raise SsmError("ssm_prefill", st, lib.ssm_status_str(st).decode())
     return y, h_out, conv_out
@@ -192,10 +197,11 @@ def decode_step(x_t, dt_t, z_t, B_t, C_t, params: dict, h, conv, *, y_t=None, st
     _check(conv, "conv", (Bsz, D, CONV_W - 1), torch.float32, dev)
     _check_params(params, D, N, dev)
     y_t = torch.empty_like(x_t) if y_t is None else y_t
+    _check(y_t, "y_t", (Bsz, D), io, dev)
     d = Dims(Bsz, 1, D, N, CONV_W, _io_code(io), 0)
     p = make_params(params)
     st = lib.ssm_decode_step(ctypes.byref(d), ctypes.byref(p), _ptr(x_t), _ptr(dt_t), _ptr(z_t), _ptr(B_t),
-                             _ptr(C_t), _ptr(y_t), _ptr(h), _ptr(conv), stream_handle(stream))
+                             _ptr(C_t), _ptr(y_t), _ptr(h), _ptr(conv), stream_handle(stream, dev))
     if st != 0:
         raise SsmError("ssm_decode_step", st, lib.ssm_status_str(st).decode())
     return y_t
@@ -229,11 +235,12 @@ def prefill_pool(x, dt, z, Bm, Cm, params: dict, slots, h_pool, conv_pool, *, se
     _check(conv_pool, "conv_pool", (S, D, CONV_W - 1), torch.float32, dev)
     _check_params(params, D, N, dev)
     y = torch.empty_like(x) if y is None else y
+    _check(y, "y", (Bsz, D, L), io, dev)
     d = Dims(Bsz, L, D, N, CONV_W, _io_code(io), chunk_hint)
     p = make_params(params)
     st = lib.ssm_prefill_pool(ctypes.byref(d), ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(z), _ptr(Bm), _ptr(Cm),
                               _ptr(seqlens), _ptr(slots), S, int(bool(resume)), _ptr(y), _ptr(h_pool),
-                              _ptr(conv_pool), stream_handle(stream))
+                              _ptr(conv_pool), stream_handle(stream, dev))
     if st != 0:
         raise SsmError("ssm_prefill_pool", st, lib.ssm_status_str(st).decode())
     return y
@@ -255,11 +262,12 @@ def decode_step_pool(x_t, dt_t, z_t, B_t, C_t, params: dict, slots, h_pool, conv
     _check(conv_pool, "conv_pool", (S, D, CONV_W - 1), torch.float32, dev)
     _check_params(params, D, N, dev)
     y_t = torch.empty_like(x_t) if y_t is None else y_t
+    _check(y_t, "y_t", (Bsz, D), io, dev)
     d = Dims(Bsz, 1, D, N, CONV_W, _io_code(io), 0)
     p = make_params(params)
     st = lib.ssm_decode_step_pool(ctypes.byref(d), ctypes.byref(p), _ptr(x_t), _ptr(dt_t), _ptr(z_t), _ptr(B_t),
                                   _ptr(C_t), _ptr(slots), S, _ptr(y_t), _ptr(h_pool), _ptr(conv_pool),
-                                  stream_handle(stream))
+                                  stream_handle(stream, dev))
     if st != 0:
         raise SsmError("ssm_decode_step_pool", st, lib.ssm_status_str(st).decode())
     return y_t
@@ -289,7 +297,8 @@ def q8_quantize(x, block: int = 128, *, q=None, scales=None, stream=None):
         scales = torch.empty(max(nb, 1), dtype=torch.float32, device=x.device)
     _check(q, "q", (n,), torch.int8, x.device)
     _check(scales, "scales", (max(nb, 1),), torch.float32, x.device)
-    st = lib.ssm_q8_quantize(n, block, _io_code(x.dtype), _ptr(x), _ptr(q), _ptr(scales), stream_handle(stream))
+    st = lib.ssm_q8_quantize(n, block, _io_code(x.dtype), _ptr(x), _ptr(q), _ptr(scales),
+                             stream_handle(stream, x.device))
     if st != 0:
         raise SsmError("ssm_q8_quantize", st, lib.ssm_status_str(st).decode())
     return q, scales
@@ -312,7 +321,7 @@ def q8_dequant_sum(q_parts, scale_parts, block: int = 128, dtype=torch.bfloat16,
     _check(y, "y", (n,), dtype, dev)
     qa = (ctypes.c_void_p * parts)(*[t.data_ptr() for t in q_parts])
     sa = (ctypes.c_void_p * parts)(*[t.data_ptr() for t in scale_parts])
-    st = lib.ssm_q8_dequant_sum(n, block, _io_code(dtype), parts, qa, sa, _ptr(y), stream_handle(stream))
+    st = lib.ssm_q8_dequant_sum(n, block, _io_code(dtype), parts, qa, sa, _ptr(y), stream_handle(stream, dev))
     if st != 0:
         raise SsmError("ssm_q8_dequant_sum", st, lib.ssm_status_str(st).decode())
     return y
@@ -370,7 +379,7 @@ class Projector:
         _check(w, "w", (M, K), x.dtype, x.device)
         _check(out, "out", shape, out_dtype, x.device)
         st = lib.ssm_proj(self.handle, kind, Bn, L, K, M, _io_code(x.dtype), _io_code(out_dtype), _ptr(x), _ptr(w),
-                          _ptr(out), _ptr(self.ws), self.ws_bytes, stream_handle(stream))
+                          _ptr(out), _ptr(self.ws), self.ws_bytes, stream_handle(stream, x.device))
         if st != 0:
             raise SsmError("ssm_proj", st, lib.ssm_status_str(st).decode())
         return out
@@ -387,7 +396,8 @@ def conv_silu(x, params: dict, conv0=None, *, u=None, stream=None):
     d = Dims(Bn, L, D, 1, CONV_W, _io_code(x.dtype), 0)
     p = Params(None, None, None, params["conv_w"].data_ptr(),
                None if params.get("conv_b") is None else params["conv_b"].data_ptr())
-    st = lib.ssm_conv_silu(ctypes.byref(d), ctypes.byref(p), _ptr(x), _ptr(conv0), _ptr(u), stream_handle(stream))
+    st = lib.ssm_conv_silu(ctypes.byref(d), ctypes.byref(p), _ptr(x), _ptr(conv0), _ptr(u),
+                           stream_handle(stream, x.device))
     if st != 0:
         raise SsmError("ssm_conv_silu", st, lib.ssm_status_str(st).decode())
     return u
@@ -415,7 +425,7 @@ def conv_xproj(x, params: dict, w, rank: int, conv0=None, *, lowrank=None, Bm=No
     p = Params(None, None, None, params["conv_w"].data_ptr(),
                None if params.get("conv_b") is None else params["conv_b"].data_ptr())
     st = lib.ssm_conv_xproj(ctypes.byref(d), ctypes.byref(p), _ptr(x), _ptr(conv0), _ptr(w), rank,
-                            _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), stream_handle(stream))
+                            _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), stream_handle(stream, x.device))
     if st != 0:
         raise SsmError("ssm_conv_xproj", st, lib.ssm_status_str(st).decode())
     return tuple(outs)

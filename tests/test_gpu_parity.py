@@ -202,6 +202,20 @@ def test_error_paths_with_real_tensors():
     with pytest.raises(ssm.SsmError) as e:
         ssm.prefill(x_mis, s["dt"], s["z"], s["Bm"], s["Cm"], prm)
     assert e.value.status == 4
+    # given outputs of the wrong size are refused by the binding before any launch
+    with pytest.raises(ValueError):
+        ssm.prefill(s["x"], s["dt"], s["z"], s["Bm"], s["Cm"], prm, y=torch.empty(B, D, L - 8, dtype=torch.bfloat16,
+                                                                                   device=DEV))
+    with pytest.raises(ValueError):
+        ssm.prefill(s["x"], s["dt"], s["z"], s["Bm"], s["Cm"], prm, h_out=torch.empty(B, D, N - 1, device=DEV))
+    with pytest.raises(TypeError):
+        ssm.prefill(s["x"], s["dt"], s["z"], s["Bm"], s["Cm"], prm, conv_out=torch.empty(B, D, 3, device=DEV,
+                                                                                          dtype=torch.float64))
+    tok = dev(I.make_decode_token(B, D, N, 0, "bf16"))
+    h, c = torch.zeros(B, D, N, device=DEV), torch.zeros(B, D, 3, device=DEV)
+    with pytest.raises(ValueError):
+        ssm.decode_step(tok["x"], tok["dt"], tok["z"], tok["Bm"], tok["Cm"], prm, h, c,
+                        y_t=torch.empty(B, D // 2, dtype=torch.bfloat16, device=DEV))
 
 
 WINDOWED = [
