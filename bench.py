@@ -95,6 +95,33 @@ def decode_bytes(B, D, N, es):
     return B * D * (2 * (N + CONV_W - 1) * 4 + 4 * es) + D * (N + 7) * 4 + B * 2 * N * es
 
 
+def timed_steps(step, nevents, warmup, steps):
+    """Run `warmup` untimed calls of step(events), then `steps` timed ones between
+    torch.cuda.synchronize() calls.  Every call's HIP events are created before the first call
+    and Python's garbage collector is paused meanwhile, so no host-side stall (an event
+    creation, a collection) can fall between two recorded events while the GPU waits for the
+    next launch.  Returns (the timed calls' events, wall seconds of the timed calls)."""
+    import gc
+
+    import torch
+
+    evs = [[TimingEvent() for _ in range(nevents)] for _ in range(warmup + steps)]
+    gc.collect()
+    gc.disable()
+    try:
+        for i in range(warmup):
+            step(evs[i])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(warmup, warmup + steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    finally:
+        gc.enable()
+    return evs[warmup:], t1 - t0
+
+
 # The sources each measured kernel is built from: a traffic record stays valid while these
 # files are unchanged (a change elsewhere in the library does not touch that kernel).
 KERNEL_SOURCES = {
@@ -353,27 +380,16 @@ def bench_codec(args):
         log("bench: copy calibration: 1 GiB read + 1 GiB written")
         del src, dst
     stream = torch.cuda.current_stream()
-    ev = TimingEvent
 
-    def step(marks):
-        e0, e1, e2 = ev(), ev(), ev()
-        e0.record(stream)
+    def step(e):
+        e[0].record(stream)
         ssm.q8_quantize(xs[0], block, q=qs[0], scales=ss[0], stream=stream)
-        e1.record(stream)
+        e[1].record(stream)
         ssm.q8_dequant_sum(qs, ss, block, xs[0].dtype, y=y, stream=stream)
-        e2.record(stream)
-        marks.append((e0, e1, e2))
+        e[2].record(stream)
 
-    warm = []
-    for _ in range(args.warmup):
-        step(warm)
-    torch.cuda.synchronize()
-    marks = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(marks)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    marks, secs = timed_steps(step, 3, args.warmup, args.steps)
+    t0, t1 = 0.0, secs
     q_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / len(marks)
     d_ms = sum(b.elapsed_time(c) for _, b, c in marks) / len(marks)
     qb, db = codec_bytes(n, nb, es, P)
@@ -429,24 +445,14 @@ def bench_layer(args):
     plan = layer.stages(hidden, wts, prm, pj, bufs, stream)
     names = [n for n, _ in plan]
 
-    def step(marks):
-        evs = [TimingEvent() for _ in range(len(names) + 1)]
+    def step(evs):
         evs[0].record(stream)
         for i, (_, f) in enumerate(plan):
             f()
             evs[i + 1].record(stream)
-        marks.append(evs)
 
-    warm = []
-    for _ in range(args.warmup):
-        step(warm)
-    torch.cuda.synchronize()
-    marks = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(marks)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    marks, secs = timed_steps(step, len(names) + 1, args.warmup, args.steps)
+    t0, t1 = 0.0, secs
     ms = [sum(m[i].elapsed_time(m[i + 1]) for m in marks) / len(marks) for i in range(len(names))]
     total = sum(ms)
     tokens = B * L
@@ -632,8 +638,8 @@ def main():
             decode_loop()
         torch.cuda.synchronize()
 
-    def step(marks):
-        e0, e1, e2 = ev(), ev(), ev()
+    def step(e):
+        e0, e1, e2 = e
         if scrub is not None:  # cold: 1 GiB written (4x the last-level cache) before the timed region
             scrub.fill_(0.0)
         e0.record(stream)
@@ -649,18 +655,9 @@ def main():
         else:
             decode_loop(stream)
         e2.record(stream)
-        marks.append((e0, e1, e2))
 
-    warm = []
-    for _ in range(args.warmup):
-        step(warm)
-    torch.cuda.synchronize()
-    marks = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(marks)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    marks, secs = timed_steps(step, 3, args.warmup, args.steps)
+    t0, t1 = 0.0, secs
 
     eager_us = None
     if T:  # eager decode loop (one host call per step), for reference
