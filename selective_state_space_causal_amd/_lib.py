@@ -47,8 +47,8 @@ def load(path: str = LIB_PATH):
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
-                          "(or python selective_state_space_causal_amd/build.py)")
+        raise ImportError(f"{path} is not built; run python selective_state_space_causal_amd/build.py "
+                          "(hipcc for gfx950)")
     lib = ctypes.CDLL(path)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.ssm_abi_version.restype = ctypes.c_int
