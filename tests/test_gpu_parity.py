@@ -298,3 +298,56 @@ def test_launch_shapes_agree_bitwise():
             torch.cuda.synchronize()
             assert torch.equal(yb[0].view(torch.int16), y[b, :n].view(torch.int16)), (b, n)
             assert torch.equal(hb[0], h[b, :n]) and torch.equal(cb[0], c[b, :n]), (b, n)
+
+
+# The method's degenerate regimes, each against the oracle through both prefill decompositions
+# and a few decode steps:
+#   a_near_zero  A = -1e-12: exp(delta A) rounds to 1 in fp32, so the state is a running sum;
+#   a_huge       A = -1e6: exp(delta A) underflows to 0, so each token's state forgets the past;
+#   a_mixed      A[c, n] from -1e-12 to -1e6 across the states of a channel;
+#   dt_tiny      dt = -60: delta = softplus(...) ~ 1e-28, the step is nearly the identity;
+#   dt_huge      dt = +60: delta ~ 55-60, large steps with full decay;
+#   x_zero       x = 0 with a conv bias: u is the same constant at every token.
+REGIMES = ["a_near_zero", "a_huge", "a_mixed", "dt_tiny", "dt_huge", "x_zero"]
+
+
+def _regime(name, prm, seq):
+    prm, seq = dict(prm), dict(seq)
+    D, N = prm["A"].shape
+    if name == "a_near_zero":
+        prm["A"] = torch.full((D, N), -1e-12, dtype=torch.float32)
+    elif name == "a_huge":
+        prm["A"] = torch.full((D, N), -1e6, dtype=torch.float32)
+    elif name == "a_mixed":
+        mags = torch.logspace(-12, 6, N, dtype=torch.float64).to(torch.float32)
+        prm["A"] = (-mags).repeat(D, 1).contiguous()
+    elif name in ("dt_tiny", "dt_huge"):
+        seq["dt"] = torch.full_like(seq["dt"], -60.0 if name == "dt_tiny" else 60.0)
+    elif name == "x_zero":
+        seq["x"] = torch.zeros_like(seq["x"])
+        prm["conv_b"] = torch.full((D,), 0.3, dtype=torch.float32)
+    return prm, seq
+
+
+@pytest.mark.parametrize("chunk_hint", [0, 1])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("regime", REGIMES)
+def test_degenerate_regimes(regime, io, chunk_hint):
+    B, L, D, N, T = 2, 600, 24, 16, 3  # L: one full 512-token window and a ragged one
+    note(f"regime {regime} {io} chunk_hint={chunk_hint}")
+    prm, seq = _regime(regime, I.make_params(D, N, seed=17), I.make_sequence(B, L, D, N, io, seed=17))
+    y, h, c = run(seq, prm, chunk_hint=chunk_hint)
+    torch.cuda.synchronize()
+    yr, hr, cr = oracle.prefill(seq, prm, nthreads=threads())
+    assert_close(y, yr, TAU[io], f"{regime} y")
+    assert_close(h, hr, TAU[io], f"{regime} h")
+    assert_bitwise(c, cr, f"{regime} conv")
+    pd = dev(prm)
+    for t in range(T):
+        _, tok = _regime(regime, prm, I.make_decode_token(B, D, N, t, io, seed=17))
+        td = dev(tok)
+        yt = ssm.decode_step(td["x"], td["dt"], td["z"], td["Bm"], td["Cm"], pd, h, c)
+        yrt, hr, cr = oracle.decode_step(tok, prm, hr, cr)
+        assert_close(yt, yrt, TAU[io], f"{regime} decode y step {t}")
+        assert_close(h, hr, TAU[io], f"{regime} decode h step {t}")
+        assert_bitwise(c, cr, f"{regime} decode conv step {t}")
