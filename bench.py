@@ -800,9 +800,10 @@ def main():
                      "flops_per_element": flops_per_element(N), "traffic": traffic,
                      "valu_issue_busy": issue_from_profiles(w.name)},
     }
-    # Not in the pool form, on mamba2.8b itself (its line is that measurement), when the decode
-    # step count is overridden (the counter runs) or when asked not to.
-    if not (args.pool or w.name == "mamba2.8b" or args.decode_steps is not None or args.no_decode_at_scale):
+    # With the decode measurement only (not on prefill-only workloads), not in the pool form, not
+    # on mamba2.8b itself (its line is that measurement), not when the decode step count is
+    # overridden (the counter runs) and not when asked not to.
+    if T and not (args.pool or w.name == "mamba2.8b" or args.decode_steps is not None or args.no_decode_at_scale):
         rec["decode_at_scale"] = decode_at_scale(args, copy_gbps)
     if args.pool and not args.no_cpu_baseline:
         log("bench: the CPU baseline is defined on the full workload; skipped in the pool form")

@@ -12,8 +12,9 @@
 //      to one affine pair (P, H) = (prod a_t, state reached from zero), keeping every a_t
 //      and b_t in registers;
 //   3. a Kogge-Stone scan of the pairs across the 64 lanes with DPP (row_shr 1/2/4/8,
-//      row_bcast 15/31) gives each lane the state entering its tokens, seeded with the
-//      carry of the previous window; lane 63's total becomes the next carry;
+//      row_bcast 15/31) gives each lane the state entering its tokens; the carry of the
+//      previous window enters through lane 0's first token, and lane 63's total becomes the
+//      next carry;
 //   4. each lane replays its K tokens from that state with the stored a_t / b_t (no second
 //      exp) and accumulates y_t = C_t . h_t.
 // B and C are shared by every channel of a batch row, so the waves of a workgroup (W
@@ -68,10 +69,14 @@ __device__ __forceinline__ float dpp(float old, float src) {
 // row 1 and row 2's into row 3 (row_bcast 15), then rows 0-1 into rows 2 and 3
 // (row_bcast 31).  Each step is H += H_src * P; P *= P_src with the DPP source folded into
 // the VALU op; a lane without a source (or in a masked-off row) is not written, which is
-// the identity (1, 0).  Then, with the window's entry state `carry` (uniform):
-//   hin   = state entering this lane's tokens = (lane i-1's composed map)(carry),
-//   carry = state after the window = (lane 63's composed map)(carry).
-// The four states are interleaved, so every DPP source was written at least eight
+// the identity (1, 0).  The window's entry state was already folded into lane 0's first
+// token (seed_carry), so after the scan H is the state after each lane's tokens, and the
+// last step needs no P.  Then:
+//   hin   = state entering this lane's tokens = H of lane i-1, and 0 for lane 0 (its tokens
+//           carry the entry state themselves; bound_ctrl:0 is this assembler's spelling of
+//           the zero-fill bit for lanes without a source),
+//   carry = state after the window = H of lane 63.
+// The four states are interleaved, so every DPP source was written at least three
 // instructions earlier; the leading s_nop covers values written just before the block.
 #define SSM_SCAN_STEP(CTRL)                                       \
   "v_fmac_f32_dpp %[H0], %[H0], %[P0] " CTRL " bank_mask:0xf\n"   \
@@ -82,9 +87,13 @@ __device__ __forceinline__ float dpp(float old, float src) {
   "v_mul_f32_dpp %[P1], %[P1], %[P1] " CTRL " bank_mask:0xf\n"    \
   "v_mul_f32_dpp %[P2], %[P2], %[P2] " CTRL " bank_mask:0xf\n"    \
   "v_mul_f32_dpp %[P3], %[P3], %[P3] " CTRL " bank_mask:0xf\n"
+#define SSM_SCAN_LAST(CTRL)                                       \
+  "v_fmac_f32_dpp %[H0], %[H0], %[P0] " CTRL " bank_mask:0xf\n"   \
+  "v_fmac_f32_dpp %[H1], %[H1], %[P1] " CTRL " bank_mask:0xf\n"   \
+  "v_fmac_f32_dpp %[H2], %[H2], %[P2] " CTRL " bank_mask:0xf\n"   \
+  "v_fmac_f32_dpp %[H3], %[H3], %[P3] " CTRL " bank_mask:0xf\n"
 
 __device__ __forceinline__ void scan4(float (&P)[4], float (&H)[4], float (&carry)[4], float (&hin)[4]) {
-  float e0, e1, e2, e3;
   int s0, s1, s2, s3;
   asm volatile(
       "s_nop 1\n"
@@ -93,30 +102,20 @@ __device__ __forceinline__ void scan4(float (&P)[4], float (&H)[4], float (&carr
       SSM_SCAN_STEP("row_shr:4 row_mask:0xf")
       SSM_SCAN_STEP("row_shr:8 row_mask:0xf")
       SSM_SCAN_STEP("row_bcast:15 row_mask:0xa")
-      SSM_SCAN_STEP("row_bcast:31 row_mask:0xc")
-      "v_fma_f32 %[e0], %[P0], %[c0], %[H0]\n"
-      "v_fma_f32 %[e1], %[P1], %[c1], %[H1]\n"
-      "v_fma_f32 %[e2], %[P2], %[c2], %[H2]\n"
-      "v_fma_f32 %[e3], %[P3], %[c3], %[H3]\n"
-      "v_mov_b32 %[i0], %[c0]\n"
-      "v_mov_b32 %[i1], %[c1]\n"
-      "v_mov_b32 %[i2], %[c2]\n"
-      "v_mov_b32 %[i3], %[c3]\n"
-      "v_mov_b32_dpp %[i0], %[e0] wave_shr:1 row_mask:0xf bank_mask:0xf\n"
-      "v_mov_b32_dpp %[i1], %[e1] wave_shr:1 row_mask:0xf bank_mask:0xf\n"
-      "v_mov_b32_dpp %[i2], %[e2] wave_shr:1 row_mask:0xf bank_mask:0xf\n"
-      "v_mov_b32_dpp %[i3], %[e3] wave_shr:1 row_mask:0xf bank_mask:0xf\n"
+      SSM_SCAN_LAST("row_bcast:31 row_mask:0xc")
       "s_nop 1\n"
-      "v_readlane_b32 %[s0], %[e0], 63\n"
-      "v_readlane_b32 %[s1], %[e1], 63\n"
-      "v_readlane_b32 %[s2], %[e2], 63\n"
-      "v_readlane_b32 %[s3], %[e3], 63\n"
+      "v_mov_b32_dpp %[i0], %[H0] wave_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:0\n"
+      "v_mov_b32_dpp %[i1], %[H1] wave_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:0\n"
+      "v_mov_b32_dpp %[i2], %[H2] wave_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:0\n"
+      "v_mov_b32_dpp %[i3], %[H3] wave_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:0\n"
+      "v_readlane_b32 %[s0], %[H0], 63\n"
+      "v_readlane_b32 %[s1], %[H1], 63\n"
+      "v_readlane_b32 %[s2], %[H2], 63\n"
+      "v_readlane_b32 %[s3], %[H3], 63\n"
       "s_nop 1\n"
       : [H0] "+v"(H[0]), [H1] "+v"(H[1]), [H2] "+v"(H[2]), [H3] "+v"(H[3]), [P0] "+v"(P[0]), [P1] "+v"(P[1]),
-        [P2] "+v"(P[2]), [P3] "+v"(P[3]), [e0] "=&v"(e0), [e1] "=&v"(e1), [e2] "=&v"(e2), [e3] "=&v"(e3),
-        [i0] "=&v"(hin[0]), [i1] "=&v"(hin[1]), [i2] "=&v"(hin[2]), [i3] "=&v"(hin[3]), [s0] "=&s"(s0),
-        [s1] "=&s"(s1), [s2] "=&s"(s2), [s3] "=&s"(s3)
-      : [c0] "s"(carry[0]), [c1] "s"(carry[1]), [c2] "s"(carry[2]), [c3] "s"(carry[3]));
+        [P2] "+v"(P[2]), [P3] "+v"(P[3]), [i0] "=&v"(hin[0]), [i1] "=&v"(hin[1]), [i2] "=&v"(hin[2]),
+        [i3] "=&v"(hin[3]), [s0] "=&s"(s0), [s1] "=&s"(s1), [s2] "=&s"(s2), [s3] "=&s"(s3));
   carry[0] = __int_as_float(s0);
   carry[1] = __int_as_float(s1);
   carry[2] = __int_as_float(s2);
@@ -124,7 +123,8 @@ __device__ __forceinline__ void scan4(float (&P)[4], float (&H)[4], float (&carr
 }
 
 // The same scan over two interleaved states (the 2-state groups of the 16-channel shape).
-// Each DPP source is written four instructions before it is read.
+// Each DPP source is written at least one instruction before it is read; the s_nop 1 lines
+// cover the places where it is the instruction right before.
 #define SSM_SCAN2_STEP(CTRL)                                      \
   "v_fmac_f32_dpp %[H0], %[H0], %[P0] " CTRL " bank_mask:0xf\n"   \
   "v_fmac_f32_dpp %[H1], %[H1], %[P1] " CTRL " bank_mask:0xf\n"   \
@@ -132,7 +132,6 @@ __device__ __forceinline__ void scan4(float (&P)[4], float (&H)[4], float (&carr
   "v_mul_f32_dpp %[P1], %[P1], %[P1] " CTRL " bank_mask:0xf\n"
 
 __device__ __forceinline__ void scan2(float (&P)[2], float (&H)[2], float (&carry)[2], float (&hin)[2]) {
-  float e0, e1;
   int s0, s1;
   asm volatile(
       "s_nop 1\n"
@@ -141,25 +140,59 @@ __device__ __forceinline__ void scan2(float (&P)[2], float (&H)[2], float (&carr
       SSM_SCAN2_STEP("row_shr:4 row_mask:0xf")
       SSM_SCAN2_STEP("row_shr:8 row_mask:0xf")
       SSM_SCAN2_STEP("row_bcast:15 row_mask:0xa")
-      SSM_SCAN2_STEP("row_bcast:31 row_mask:0xc")
-      "v_fma_f32 %[e0], %[P0], %[c0], %[H0]\n"
-      "v_fma_f32 %[e1], %[P1], %[c1], %[H1]\n"
-      "v_mov_b32 %[i0], %[c0]\n"
-      "v_mov_b32 %[i1], %[c1]\n"
-      "v_mov_b32_dpp %[i0], %[e0] wave_shr:1 row_mask:0xf bank_mask:0xf\n"
-      "v_mov_b32_dpp %[i1], %[e1] wave_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_fmac_f32_dpp %[H0], %[H0], %[P0] row_bcast:31 row_mask:0xc bank_mask:0xf\n"
+      "v_fmac_f32_dpp %[H1], %[H1], %[P1] row_bcast:31 row_mask:0xc bank_mask:0xf\n"
       "s_nop 1\n"
-      "v_readlane_b32 %[s0], %[e0], 63\n"
-      "v_readlane_b32 %[s1], %[e1], 63\n"
+      "v_mov_b32_dpp %[i0], %[H0] wave_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:0\n"
+      "v_mov_b32_dpp %[i1], %[H1] wave_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:0\n"
+      "v_readlane_b32 %[s0], %[H0], 63\n"
+      "v_readlane_b32 %[s1], %[H1], 63\n"
       "s_nop 1\n"
-      : [H0] "+v"(H[0]), [H1] "+v"(H[1]), [P0] "+v"(P[0]), [P1] "+v"(P[1]), [e0] "=&v"(e0), [e1] "=&v"(e1),
-        [i0] "=&v"(hin[0]), [i1] "=&v"(hin[1]), [s0] "=&s"(s0), [s1] "=&s"(s1)
-      : [c0] "s"(carry[0]), [c1] "s"(carry[1]));
+      : [H0] "+v"(H[0]), [H1] "+v"(H[1]), [P0] "+v"(P[0]), [P1] "+v"(P[1]), [i0] "=&v"(hin[0]),
+        [i1] "=&v"(hin[1]), [s0] "=&s"(s0), [s1] "=&s"(s1));
   carry[0] = __int_as_float(s0);
   carry[1] = __int_as_float(s1);
 }
 #undef SSM_SCAN2_STEP
+#undef SSM_SCAN_LAST
 #undef SSM_SCAN_STEP
+
+// Fold the window's entry state into lane 0's first token: b_0 += a_0 * carry on lane 0 only
+// (exec narrowed to lane 0 and restored inside the block; lane 0 stays off if it was off), so
+// the lane scan and the replay carry it with no further term.  A DPP instruction needs five
+// wait states after an exec write; the next one (the lane scan) comes after the seven fold
+// FMAs per state that depend on this block's results.
+#define SSM_SEED(I) "v_fmac_f32 %[b" #I "], %[c" #I "], %[a" #I "]\n"
+__device__ __forceinline__ void seed4(float* b, const float* a, const float* c) {
+  uint64_t save;
+  asm volatile("s_mov_b64 %[sv], exec\n"
+               "s_and_b64 exec, %[sv], 1\n"
+               SSM_SEED(0) SSM_SEED(1) SSM_SEED(2) SSM_SEED(3)
+               "s_mov_b64 exec, %[sv]\n"
+               : [b0] "+v"(b[0]), [b1] "+v"(b[1]), [b2] "+v"(b[2]), [b3] "+v"(b[3]), [sv] "=&s"(save)
+               : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [c0] "s"(c[0]), [c1] "s"(c[1]),
+                 [c2] "s"(c[2]), [c3] "s"(c[3]));
+}
+__device__ __forceinline__ void seed2(float* b, const float* a, const float* c) {
+  uint64_t save;
+  asm volatile("s_mov_b64 %[sv], exec\n"
+               "s_and_b64 exec, %[sv], 1\n"
+               SSM_SEED(0) SSM_SEED(1)
+               "s_mov_b64 exec, %[sv]\n"
+               : [b0] "+v"(b[0]), [b1] "+v"(b[1]), [sv] "=&s"(save)
+               : [a0] "v"(a[0]), [a1] "v"(a[1]), [c0] "s"(c[0]), [c1] "s"(c[1]));
+}
+#undef SSM_SEED
+
+template <int G>
+__device__ __forceinline__ void seed_carry(float (&b0)[G], const float (&a0)[G], const float (&carry)[G]) {
+  if constexpr (G == 2) {
+    seed2(b0, a0, carry);
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; g += 4) seed4(&b0[g], &a0[g], &carry[g]);
+  }
+}
 
 // Scan G interleaved states (G = 2, or a multiple of 4).
 template <int G>
@@ -482,6 +515,9 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
         P[q] = hw_exp2(A2[q0 + q] * dsum);  // prod_j exp(delta_j A) over this lane's tokens
         H[q] = 0.0f;
       }
+      float hc[G], cg[G];
+#pragma unroll
+      for (int q = 0; q < G; ++q) cg[q] = carry[q0 + q];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         float bq[G];
@@ -490,12 +526,11 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
         for (int q = 0; q < G; ++q) {
           av[j][q] = hw_exp2(dl[j] * A2[q0 + q]);
           bv[j][q] = du[j] * bq[q];
-          H[q] = fmaf(av[j][q], H[q], bv[j][q]);
         }
-      }
-      float hc[G], cg[G];
+        if (j == 0) seed_carry<G>(bv[0], av[0], cg);
 #pragma unroll
-      for (int q = 0; q < G; ++q) cg[q] = carry[q0 + q];
+        for (int q = 0; q < G; ++q) H[q] = fmaf(av[j][q], H[q], bv[j][q]);
+      }
       scan_group<G>(P, H, cg, hc);
 #pragma unroll
       for (int q = 0; q < G; ++q) carry[q0 + q] = cg[q];
