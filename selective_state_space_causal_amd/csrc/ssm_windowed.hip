@@ -488,21 +488,26 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
 
     float dl[K], du[K], yv[K];
     float dsum = 0.0f;
+    // Past the row end the step is an identity: softplus(-inf) is exactly 0.  Only a window
+    // that reaches past the end needs the per-token selection (a uniform branch picks it).
+    auto front = [&](auto masked) {
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const float s3 = j >= 3 ? xv[j - 3] : (j == 0 ? xm3 : (j == 1 ? xm2 : xm1));
-      const float s2 = j >= 2 ? xv[j - 2] : (j == 0 ? xm2 : xm1);
-      const float s1 = j >= 1 ? xv[j - 1] : xm1;
-      const float v = fmaf(w3, xv[j], fmaf(w2, s1, fmaf(w1, s2, fmaf(w0, s3, cb))));
-      const float u = silu(v);
-      // Past the row end the step is an identity: softplus(-inf) is exactly 0.  Selecting the
-      // argument (not the result) keeps this branch-free.
-      const float d = softplus(j < nvalid ? unpack<IO>(cdt.w, j) + dtb : -__builtin_inff());
-      dl[j] = d;
-      du[j] = d * u;
-      yv[j] = dsk * u;
-      dsum += d;
-    }
+      for (int j = 0; j < K; ++j) {
+        const float s3 = j >= 3 ? xv[j - 3] : (j == 0 ? xm3 : (j == 1 ? xm2 : xm1));
+        const float s2 = j >= 2 ? xv[j - 2] : (j == 0 ? xm2 : xm1);
+        const float s1 = j >= 1 ? xv[j - 1] : xm1;
+        const float v = fmaf(w3, xv[j], fmaf(w2, s1, fmaf(w1, s2, fmaf(w0, s3, cb))));
+        const float u = silu(v);
+        const float arg = unpack<IO>(cdt.w, j) + dtb;
+        const float d = softplus(decltype(masked)::value && j >= nvalid ? -__builtin_inff() : arg);
+        dl[j] = d;
+        du[j] = d * u;
+        yv[j] = dsk * u;
+        dsum += d;
+      }
+    };
+    if (rem == WIN) front(std::integral_constant<bool, false>{});
+    else front(std::integral_constant<bool, true>{});
 
     // ---- state groups: local pairs, lane scan, replay ----
     const float* tb = &tile.B[lane * LANE_STRIDE];
