@@ -180,7 +180,9 @@ def record_issue(csv_path, workload):
     summed over waves): the share of each SIMD's issue slots, over the kernel's duration, in
     which one of its waves issued a VALU instruction (a transcendental holds two slots).  The
     kernel's duration is taken as a wave's lifetime, which holds when every wave is resident
-    from start to end (one round, as for slice7b's 2048 waves on 1024 SIMDs)."""
+    from start to end (one round, as for slice7b's 2048 waves on 1024 SIMDs).  The run's first
+    prefill dispatch is its warm-up call, which bench.py also leaves out of its timing (it runs
+    ~8% longer, on caches and translations not yet warm): it is left out here too."""
     import csv
     from collections import defaultdict
 
@@ -193,11 +195,15 @@ def record_issue(csv_path, workload):
         per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
     if not per:
         raise SystemExit(f"no prefill dispatch in {csv_path}")
+    order = sorted(per, key=int)
+    if len(order) > 1:
+        per = {k: per[k] for k in order[1:]}
     mean = lambda k: sum(d[k] for d in per.values()) / len(per)
     waves, cycles, active = mean("SQ_WAVES"), mean("SQ_WAVE_CYCLES"), mean("SQ_ACTIVE_INST_VALU")
     if waves > MI355X_SIMDS * 2:
         raise SystemExit("more than two waves per SIMD: waves are not all resident at once")
-    issue = {"kernel": name, "dispatches": len(per), "source_hash": kernel_source_hash("scan"),
+    issue = {"kernel": name, "dispatches": len(per), "warmup_dispatches_left_out": len(order) - len(per),
+             "source_hash": kernel_source_hash("scan"),
              "command": SQ_COMMAND.format(tag=os.path.basename(csv_path).split("_counter")[0], workload=workload),
              "waves": int(waves), "wave_cycles_per_wave": round(cycles / waves, 1),
              "active_inst_valu_per_wave": round(active / waves, 1),
