@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void decode_quad(ScanArgs a) {
   const int64_t rows = a.B * a.D;
   const int64_t row = min(gid >> 2, rows - 1);  // a ragged tail repeats the last channel, writes nothing
   const int q = (int)(gid & 3);
-  const int64_t b = row / a.D, c = row - b * a.D;
+  const int64_t b = (int64_t)(((uint64_t)row * a.d_magic) >> a.d_shift), c = row - b * a.D;
   int64_t crow;  // cache (h / conv) row; a skipped batch row leaves as a whole quad (no DPP partner lost)
   if (!cache_row(a, b, c, crow)) return;
   const bool live = (gid >> 2) < rows;
@@ -78,7 +78,9 @@ __global__ __launch_bounds__(256) void decode_quad(ScanArgs a) {
 
 bool decode_quad_supported(const ScanArgs& a) { return a.N == 16; }
 
-hipError_t launch_decode_quad(const ScanArgs& a, hipStream_t s) {
+hipError_t launch_decode_quad(const ScanArgs& a_in, hipStream_t s) {
+  ScanArgs a = a_in;
+  div_magic(a.D, &a.d_magic, &a.d_shift);  // rows per launch stay below 2^30
   const int64_t lanes = a.B * a.D * 4;
   const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
   if (a.bf16) decode_quad<bf16_t><<<grid, block, 0, s>>>(a);

@@ -33,7 +33,24 @@ struct ScanArgs {
   const int32_t* seqlens;  // [B] tokens of each batch row to run (clamped to [0, L]); null: all L
   const int32_t* slots;    // [B] cache-pool entry of each batch row; outside [0, pool) skips the row
   int64_t pool;            // entries of the cache pool when slots is set
+  // Division by D for indices n < 2^30: n / D = (n * d_magic) >> d_shift (set by the decode
+  // launcher; see div_magic).
+  uint64_t d_magic;
+  int d_shift;
 };
+
+// Multiply-shift constants for unsigned division by d (1 <= d <= 2^24) of any n < 2^30: with
+// l = ceil(log2 d), m = ceil(2^(30 + l) / d) is below 2^31 + 1 and floor(n m / 2^(30 + l)) =
+// floor(n / d), because m = (2^(30 + l) + e) / d with 0 <= e < d <= 2^l, so the excess
+// n e / (d 2^(30 + l)) stays below 1 / d (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994).
+inline void div_magic(int64_t d, uint64_t* magic, int* shift) {
+  int l = 0;
+  while ((int64_t(1) << l) < d) ++l;
+  const int s = 30 + l;
+  *magic = ((uint64_t(1) << s) + uint64_t(d) - 1) / uint64_t(d);
+  *shift = s;
+}
 
 // Cache row (h / conv entry) of channel c of batch row b, or false when the row is skipped.
 __device__ __forceinline__ bool cache_row(const ScanArgs& a, int64_t b, int64_t c, int64_t& crow) {
