@@ -46,6 +46,9 @@ __global__ __launch_bounds__(256) void decode_quad(ScanArgs a) {
   const IO* Ct = static_cast<const IO*>(a.Cm) + b * 16 + q * QS;
   const float xt = to_f32(static_cast<const IO*>(a.x)[row]);
   const float dtr = to_f32(static_cast<const IO*>(a.dt)[row]);
+  // z is read with the other inputs (x stands in when there is no gate) and the gate applied as
+  // a select, so the step waits for one memory round trip, not a second one for z at the end.
+  const float zt = to_f32(static_cast<const IO*>(a.z ? a.z : a.x)[row]);
 
   const float v = cb + w.x * x0 + w.y * x1 + w.z * x2 + w.w * xt;
   const float u = silu(v);
@@ -60,9 +63,13 @@ __global__ __launch_bounds__(256) void decode_quad(ScanArgs a) {
     h[n] = fmaf(dA, h[n], du * to_f32(Bt[n]));
     r = fmaf(to_f32(Ct[n]), h[n], r);
   }
+  // Keep the D-skip and gate inputs out of the store branch below: the compiler would otherwise
+  // sink their loads into it, after the quad sum, and the step would wait for memory twice.
+  asm volatile("" ::"v"(dsk), "v"(zt));
   r = quad_sum(r);
   r = fmaf(dsk, u, r);
-  if (a.z) r *= silu(to_f32(static_cast<const IO*>(a.z)[row]));
+  const float gz = silu(zt);
+  r *= a.z ? gz : 1.0f;
   if (!live) return;
   *reinterpret_cast<float4*>(a.h_out + crow * 16 + q * QS) = make_float4(h[0], h[1], h[2], h[3]);
   if (q == 0) {
