@@ -139,3 +139,45 @@ def test_quantize_past_the_grid_cap():
         assert np.array_equal(q[e0:e1].cpu().numpy(), qr), e0
         got = sc[e0 // block:e0 // block + len(sr)].cpu().numpy()
         assert np.array_equal(got.view(np.uint32), sr.view(np.uint32)), e0
+
+
+def _decode_rows_case(Bn, Dn, check, seed):
+    """One decode step over Bn batch rows of Dn channels (tokens drawn on the device), checked on
+    whole rows against the oracle.  The decode kernel finds each quad's batch row and channel with
+    a multiply-shift division by Dn; these cases put large quotients (many rows per launch) and
+    large, odd divisors through it, on both sides of a launch split."""
+    N = 16
+    note(f"decode rows B={Bn} D={Dn} (launch split every {(1 << 31) // (64 * (Dn + 16))} rows)")
+    prm = I.make_params(Dn, N, seed=seed)
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    bf = torch.bfloat16
+    tok = {"x": torch.randn(Bn, Dn, generator=g, device=DEV).to(bf),
+           "dt": (0.5 * torch.randn(Bn, Dn, generator=g, device=DEV)).to(bf),
+           "z": torch.randn(Bn, Dn, generator=g, device=DEV).to(bf),
+           "Bm": torch.randn(Bn, N, generator=g, device=DEV).to(bf),
+           "Cm": torch.randn(Bn, N, generator=g, device=DEV).to(bf)}
+    h = torch.randn(Bn, Dn, N, generator=g, device=DEV)
+    c = torch.randn(Bn, Dn, 3, generator=g, device=DEV).to(bf).float()
+    h_in = {b: f64(h[b]) for b in check}
+    c_in = {b: f64(c[b]) for b in check}
+    y = ssm.decode_step(tok["x"], tok["dt"], tok["z"], tok["Bm"], tok["Cm"], dev(prm), h, c)
+    torch.cuda.synchronize()
+    for b in check:
+        tb = {k: v[b:b + 1].cpu() for k, v in tok.items()}
+        yr, hr, cr = oracle.decode_step(tb, prm, h_in[b][None], c_in[b][None])
+        assert_close(y[b], yr[0], TAU["bf16"], f"row {b} y")
+        assert_close(h[b], hr[0], TAU["bf16"], f"row {b} h")
+        assert_bitwise(c[b], cr[0], f"row {b} conv")
+
+
+def test_decode_large_odd_divisor():
+    Dn = (1 << 20) + 1
+    per = (1 << 31) // (64 * (Dn + 16))  # 31 rows per launch
+    _decode_rows_case(40, Dn, [0, 1, per - 1, per, per + 1, 39], seed=64)
+
+
+def test_decode_small_divisor_many_rows():
+    Dn = 3
+    per = (1 << 31) // (64 * (Dn + 16))  # 1766022 rows per launch
+    Bn = per + 233979                      # two launches
+    _decode_rows_case(Bn, Dn, [0, 1, 777777, per - 1, per, per + 1, Bn - 1], seed=65)
