@@ -24,9 +24,18 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
+constexpr int kDecodeBlock = 256;  // threads per workgroup (the launch below uses exactly this)
+
 template <typename IO>
-__global__ __launch_bounds__(256) void decode_quad(ScanArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(kDecodeBlock) void decode_quad(ScanArgs a) {
+  // Every argument the step reads, fetched in one batch of scalar loads before any arithmetic.
+  // Left to itself the compiler loads the tensor pointers in a second batch after the index
+  // arithmetic, and each graph node's arguments come from memory not yet in the scalar cache,
+  // so the step waited for two scalar round trips before its first vector load.
+  asm volatile("" ::"s"(a.x), "s"(a.dt), "s"(a.z), "s"(a.Bm), "s"(a.Cm), "s"(a.A), "s"(a.Dskip), "s"(a.dt_bias),
+               "s"(a.conv_w), "s"(a.conv_b), "s"(a.h0), "s"(a.conv0), "s"(a.y), "s"(a.h_out), "s"(a.conv_out),
+               "s"(a.B), "s"(a.D), "s"(a.slots), "s"(a.pool), "s"(a.d_magic), "s"(a.d_shift));
+  const int64_t gid = (int64_t)blockIdx.x * kDecodeBlock + threadIdx.x;
   const int64_t rows = a.B * a.D;
   const int64_t row = min(gid >> 2, rows - 1);  // a ragged tail repeats the last channel, writes nothing
   const int q = (int)(gid & 3);
@@ -89,7 +98,7 @@ hipError_t launch_decode_quad(const ScanArgs& a_in, hipStream_t s) {
   ScanArgs a = a_in;
   div_magic(a.D, &a.d_magic, &a.d_shift);  // rows per launch stay below 2^30
   const int64_t lanes = a.B * a.D * 4;
-  const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+  const dim3 grid((unsigned)((lanes + kDecodeBlock - 1) / kDecodeBlock)), block(kDecodeBlock);
   if (a.bf16) decode_quad<bf16_t><<<grid, block, 0, s>>>(a);
   else decode_quad<float><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
