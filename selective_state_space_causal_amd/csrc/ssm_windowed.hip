@@ -536,7 +536,12 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
 #pragma unroll
         for (int q = 0; q < G; ++q) H[q] = fmaf(av[j][q], H[q], bv[j][q]);
       }
+      // The lane scan is a chain of dependent DPP steps; raising the wave's issue priority for it
+      // lets the other waves of the SIMD fill the gaps with their (independent) fold and replay
+      // work instead of the reverse (3-4% faster with three or four waves per SIMD).
+      __builtin_amdgcn_s_setprio(2);
       scan_group<G>(P, H, cg, hc);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int q = 0; q < G; ++q) carry[q0 + q] = cg[q];
 #pragma unroll
