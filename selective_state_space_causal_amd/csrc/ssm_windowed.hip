@@ -506,8 +506,12 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
         dsum += d;
       }
     };
+    // With two waves per SIMD (8-state groups) the front end, too, runs at raised priority:
+    // measured 2% faster there, and ~0.5% slower with three or four waves.
+    if constexpr (G == 8) __builtin_amdgcn_s_setprio(1);
     if (rem == WIN) front(std::integral_constant<bool, false>{});
     else front(std::integral_constant<bool, true>{});
+    if constexpr (G == 8) __builtin_amdgcn_s_setprio(0);
 
     // ---- state groups: local pairs, lane scan, replay ----
     const float* tb = &tile.B[lane * LANE_STRIDE];
