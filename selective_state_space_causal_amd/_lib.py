@@ -96,7 +96,7 @@ def load(path: str = LIB_PATH):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()  # ctypes passes the integer as a void*
 
 
 def _io_code(dtype: torch.dtype) -> int:
@@ -108,16 +108,19 @@ def _io_code(dtype: torch.dtype) -> int:
 
 
 def _check(t: Optional[torch.Tensor], name: str, shape, dtype, device, optional=False):
+    """Shape, dtype, GPU device and contiguity of a tensor handed to the library (the cheap tests
+    first; messages are built only on a mismatch)."""
     if t is None:
         if optional:
             return
         raise ValueError(f"{name} is required")
+    if t.shape == shape and t.dtype == dtype and t.is_cuda and t.get_device() == device.index and t.is_contiguous():
+        return
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
         raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
-    if t.device != device or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    raise ValueError(f"{name} must be a contiguous tensor on {device} (a GPU)")
 
 
 def make_params(params: dict) -> Params:
@@ -135,11 +138,11 @@ def _check_params(params: dict, D: int, N: int, device):
     _check(params.get("conv_b"), "conv_b", (D,), f32, device, optional=True)
 
 
-def stream_handle(stream=None, device=None) -> ctypes.c_void_p:
+def stream_handle(stream=None, device=None) -> int:
     """The HIP stream to enqueue on: `stream`, else the current stream of `device` (the
     tensors' device), so kernels run where the tensors live."""
     s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return s.cuda_stream  # ctypes passes the integer as a void*
 
 
 def workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype=torch.bfloat16, chunk_hint=0) -> int:
@@ -212,7 +215,7 @@ def _check_index(t, name, B, device, optional=False):
         if optional:
             return
         raise ValueError(f"{name} is required")
-    if tuple(t.shape) != (B,) or t.dtype != torch.int32 or t.device != device or not t.is_contiguous():
+    if tuple(t.shape) != (B,) or t.dtype != torch.int32 or not t.is_cuda or t.device != device or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous int32 tensor of shape ({B},) on {device}")
 
 

@@ -192,3 +192,22 @@ def test_pool_entry_points_validation():
     assert prefill_pool(dims(), params(), seqlens=fake(8, 2)) == ALIGN
     assert prefill_pool(dims(), params(), seqlens=fake(5, 0)) == ALIAS   # y over seqlens
     assert prefill_pool(dims(chunk_hint=5), params()) == SHAPE
+
+
+def test_binding_refuses_host_tensors():
+    """Tensors in host memory are refused by the binding before any HIP call (the kernels would
+    read them as device addresses)."""
+    import torch
+
+    import selective_state_space_causal_amd as ssm
+    from selective_state_space_causal_amd import inputs as I
+
+    B, L, D, N = 1, 16, 8, 16
+    prm = I.make_params(D, N)
+    s = I.make_sequence(B, L, D, N, "bf16")
+    with pytest.raises(ValueError, match="GPU"):
+        ssm.prefill(s["x"], s["dt"], s["z"], s["Bm"], s["Cm"], prm)
+    tok = I.make_decode_token(B, D, N, 0, "bf16")
+    h, c = torch.zeros(B, D, N), torch.zeros(B, D, 3)
+    with pytest.raises(ValueError, match="GPU"):
+        ssm.decode_step(tok["x"], tok["dt"], tok["z"], tok["Bm"], tok["Cm"], prm, h, c)
