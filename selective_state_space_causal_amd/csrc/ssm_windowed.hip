@@ -244,6 +244,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// View of a row of `elems` elements from element `from` on, for one window: the window's offset
+// is in the descriptor's base (scalar arithmetic), so every access of the window addresses it
+// through its per-lane voffset alone, which the range check covers, and the view ends where the
+// row ends (an empty view when `from` is past it: loads read zeros, stores are dropped).
+// Rows hold fewer than 2^31 bytes (windowed_supported), so the counts are 32-bit scalars.
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window_rsrc(const T* row, int elems, int from) {
+  const int left = elems - from;
+  return row_rsrc(row + from, left > 0 ? left * (int)sizeof(T) : 0);
+}
+
 // Unpack io words into fp32: bf16 pairs are (low, high) halves of a dword.
 template <typename IO>
 __device__ __forceinline__ float unpack(const uint32_t* w, int j) {
@@ -273,11 +284,11 @@ template <typename IO, bool ALIGNED>
 struct Lanes {
   static constexpr int DW = K * (int)sizeof(IO) / 4;
   uint32_t w[DW];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff) {
     if constexpr (ALIGNED) {
 #pragma unroll
       for (int i = 0; i < DW; i += 4) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * i, soff, STREAM);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * i, 0, STREAM);
         w[i] = v[0];
         w[i + 1] = v[1];
         w[i + 2] = v[2];
@@ -286,21 +297,20 @@ struct Lanes {
     } else if constexpr (sizeof(IO) == 2) {
 #pragma unroll
       for (int i = 0; i < DW; ++i) {
-        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 4 * i, soff, STREAM);
-        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 4 * i + 2, soff, STREAM);
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 4 * i, 0, STREAM);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 4 * i + 2, 0, STREAM);
         w[i] = lo | (hi << 16);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < DW; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * i, soff, STREAM);
+      for (int i = 0; i < DW; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * i, 0, STREAM);
     }
   }
 };
 
 // Store the lane's first `nvalid` outputs (all K as vector stores when the lane is whole).
 template <typename IO, bool ALIGNED>
-__device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&v)[K],
-                                            int nvalid) {
+__device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, const float (&v)[K], int nvalid) {
   if (nvalid < K) {
     if (nvalid > 0) {
 #pragma unroll
@@ -308,9 +318,9 @@ __device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, 
         if (j < nvalid) {
           if constexpr (sizeof(IO) == 2)
             __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(v[j], 0.0f) & 0xFFFFu), r,
-                                                  voff + 2 * j, soff, STREAM);
+                                                  voff + 2 * j, 0, STREAM);
           else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), r, voff + 4 * j, soff, STREAM);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[j]), r, voff + 4 * j, 0, STREAM);
         }
       }
     }
@@ -322,12 +332,12 @@ __device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, 
     for (int i = 0; i < K / 2; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     if constexpr (ALIGNED) {
       const u32x4 v4 = {w[0], w[1], w[2], w[3]};
-      __builtin_amdgcn_raw_buffer_store_b128(v4, r, voff, soff, STREAM);
+      __builtin_amdgcn_raw_buffer_store_b128(v4, r, voff, 0, STREAM);
     } else {
 #pragma unroll
       for (int i = 0; i < K / 2; ++i) {
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[i] & 0xFFFFu), r, voff + 4 * i, soff, STREAM);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[i] >> 16), r, voff + 4 * i + 2, soff, STREAM);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[i] & 0xFFFFu), r, voff + 4 * i, 0, STREAM);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[i] >> 16), r, voff + 4 * i + 2, 0, STREAM);
       }
     }
   } else {
@@ -336,11 +346,11 @@ __device__ __forceinline__ void store_lanes(__amdgpu_buffer_rsrc_t r, int voff, 
       for (int i = 0; i < K; i += 4) {
         const u32x4 v4 = {__float_as_uint(v[i]), __float_as_uint(v[i + 1]), __float_as_uint(v[i + 2]),
                           __float_as_uint(v[i + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(v4, r, voff + 4 * i, soff, STREAM);
+        __builtin_amdgcn_raw_buffer_store_b128(v4, r, voff + 4 * i, 0, STREAM);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < K; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), r, voff + 4 * i, soff, STREAM);
+      for (int i = 0; i < K; ++i) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[i]), r, voff + 4 * i, 0, STREAM);
     }
   }
 }
@@ -355,12 +365,12 @@ struct TileChunks {
   static constexpr int PER_THREAD = (CHUNKS + THREADS - 1) / THREADS;
   uint32_t b[PER_THREAD][4], c[PER_THREAD][4];
 
-  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rc, int soff) {
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rc) {
 #pragma unroll
     for (int r = 0; r < PER_THREAD; ++r) {
       const int voff = (threadIdx.x + r * THREADS) * 16;
-      const auto vb = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, soff, 0);
-      const auto vc = __builtin_amdgcn_raw_buffer_load_b128(rc, voff, soff, 0);
+      const auto vb = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, 0, 0);
+      const auto vc = __builtin_amdgcn_raw_buffer_load_b128(rc, voff, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         b[r][e] = vb[e];
@@ -411,18 +421,25 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
   const int64_t L = a.L;                 // row stride of x, dt, z, y and B / C
   const int64_t cc = active ? c : 0;
   const int64_t row = b * a.D + cc;
-  const int64_t row_bytes = L * ES;
   int64_t crow;                          // cache (h / conv) row
   if (!cache_row(a, b, cc, crow)) return;  // a skipped batch row: the whole workgroup leaves together
   const int64_t Lb = row_len(a, b);      // tokens to run for this batch row
 
-  const auto rx = row_rsrc(static_cast<const IO*>(a.x) + row * L, row_bytes);
-  const auto rdt = row_rsrc(static_cast<const IO*>(a.dt) + row * L, row_bytes);
-  const auto rz = row_rsrc(a.z ? static_cast<const IO*>(a.z) + row * L : a.x, a.z ? row_bytes : 0);
-  const auto ry = row_rsrc(static_cast<IO*>(a.y) + row * L, active ? row_bytes : 0);
-  const auto rB = row_rsrc(static_cast<const IO*>(a.Bm) + b * L * NS, L * NS * ES);
-  const auto rC = row_rsrc(static_cast<const IO*>(a.Cm) + b * L * NS, L * NS * ES);
+  // Rows of the channel's streams and of the batch row's B / C; each window reads and writes
+  // them through window_rsrc views.  An idle wave's y view is empty, so it stores nothing.
   const bool gate = a.z != nullptr;
+  const IO* xrow = static_cast<const IO*>(a.x) + row * L;
+  const IO* dtrow = static_cast<const IO*>(a.dt) + row * L;
+  const IO* zrow = gate ? static_cast<const IO*>(a.z) + row * L : xrow;
+  IO* yrow = static_cast<IO*>(a.y) + row * L;
+  const int Li = (int)L;
+  const int y_elems = active ? Li : 0;
+  // B / C are viewed up to the row's own length only: a 16-byte chunk holds half a token (a
+  // quarter for fp32), so the range check reads the tokens past the end as zeros, whatever
+  // the tensors hold there (a ragged row's padding may hold anything, NaN included).
+  const IO* Brow = static_cast<const IO*>(a.Bm) + b * L * NS;
+  const IO* Crow = static_cast<const IO*>(a.Cm) + b * L * NS;
+  const int bc_elems = (int)Lb * NS;
 
   // Channel constants.
   const float w0 = a.conv_w[cc * 4 + 0], w1 = a.conv_w[cc * 4 + 1], w2 = a.conv_w[cc * 4 + 2],
@@ -447,10 +464,10 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
   const int voff = lane * K * ES;  // this lane's byte offset inside a window
   TileChunks<IO, THREADS> pf;
   Lanes<IO, ALIGNED> px, pdt, pz;
-  pf.fetch(rB, rC, 0);
-  px.load(rx, voff, 0);
-  pdt.load(rdt, voff, 0);
-  if (gate) pz.load(rz, voff, 0);
+  pf.fetch(window_rsrc(Brow, bc_elems, 0), window_rsrc(Crow, bc_elems, 0));
+  px.load(window_rsrc(xrow, Li, 0), voff);
+  pdt.load(window_rsrc(dtrow, Li, 0), voff);
+  if (gate) pz.load(window_rsrc(zrow, Li, 0), voff);
 
   pf.store(tiles[0]);
   for (int w = 0; w < nwin; ++w) {
@@ -462,10 +479,11 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
     const Lanes<IO, ALIGNED> cx = px, cdt = pdt, cz = pz;
     const bool more = w + 1 < nwin;
     if (more) {  // prefetch the next window while this one is computed
-      pf.fetch(rB, rC, (t0 + WIN) * NS * ES);
-      px.load(rx, voff, (t0 + WIN) * ES);
-      pdt.load(rdt, voff, (t0 + WIN) * ES);
-      if (gate) pz.load(rz, voff, (t0 + WIN) * ES);
+      const int t1 = t0 + WIN;
+      pf.fetch(window_rsrc(Brow, bc_elems, t1 * NS), window_rsrc(Crow, bc_elems, t1 * NS));
+      px.load(window_rsrc(xrow, Li, t1), voff);
+      pdt.load(window_rsrc(dtrow, Li, t1), voff);
+      if (gate) pz.load(window_rsrc(zrow, Li, t1), voff);
     }
     if (!active) {
       if (more) pf.store(tiles[(w + 1) & 1]);
@@ -488,20 +506,24 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
 
     float dl[K], du[K], yv[K];
     float dsum = 0.0f;
-    // Past the row end the step is an identity: softplus(-inf) is exactly 0.  Only a window
-    // that reaches past the end needs the per-token selection (a uniform branch picks it).
+    // Past the row end the step is the identity: delta is exactly 0 (softplus(-inf)) and so is
+    // the drive delta * u, selected rather than multiplied, since u there is made of whatever
+    // the tensors hold past the row (NaN and infinities included).  The tile's B there is
+    // zero too (read through the B / C views, which end at the row's length).  Only a window that reaches past the end needs this per-token
+    // selection (a uniform branch picks it).
     auto front = [&](auto masked) {
 #pragma unroll
       for (int j = 0; j < K; ++j) {
+        const bool pad = decltype(masked)::value && j >= nvalid;
         const float s3 = j >= 3 ? xv[j - 3] : (j == 0 ? xm3 : (j == 1 ? xm2 : xm1));
         const float s2 = j >= 2 ? xv[j - 2] : (j == 0 ? xm2 : xm1);
         const float s1 = j >= 1 ? xv[j - 1] : xm1;
         const float v = fmaf(w3, xv[j], fmaf(w2, s1, fmaf(w1, s2, fmaf(w0, s3, cb))));
         const float u = silu(v);
         const float arg = unpack<IO>(cdt.w, j) + dtb;
-        const float d = softplus(decltype(masked)::value && j >= nvalid ? -__builtin_inff() : arg);
+        const float d = softplus(pad ? -__builtin_inff() : arg);
         dl[j] = d;
-        du[j] = d * u;
+        du[j] = pad ? 0.0f : d * u;
         yv[j] = dsk * u;
         dsum += d;
       }
@@ -565,7 +587,7 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
       for (int j = 0; j < K; ++j) yv[j] *= silu(unpack<IO>(cz.w, j));
     }
     if (more) pf.store(tiles[(w + 1) & 1]);
-    store_lanes<IO, ALIGNED>(ry, voff, t0 * ES, yv, nvalid);
+    store_lanes<IO, ALIGNED>(window_rsrc(yrow, y_elems, t0), voff, yv, nvalid);
   }
 
   if (active && lane == 0) {

@@ -88,6 +88,45 @@ def make_params(d_inner: int, d_state: int, seed: int = 0,
             "conv_w": f(conv_w), "conv_b": f(np.zeros(D))}
 
 
+def _separated(g: np.random.Generator, n: int, lo: float, hi: float) -> np.ndarray:
+    """n values in [lo, hi], each at least 0.6 (hi - lo) / 5 away from the previous channel's
+    value and from channel 0's: [lo, hi] is cut into five bins, channel 0 takes a random bin,
+    every other channel one of the four remaining bins, never its predecessor's, and each value
+    lies in the middle 40% of its bin."""
+    w = (hi - lo) / 5.0
+    bins = np.empty(n, dtype=np.int64)
+    bins[0] = g.integers(5)
+    if n > 1:
+        others = np.array([k for k in range(5) if k != bins[0]])
+        walk = (g.integers(4) + np.cumsum(g.integers(1, 4, size=n - 1))) % 4
+        bins[1:] = others[walk]
+    return lo + w * (bins + g.uniform(0.3, 0.7, size=n))
+
+
+def make_params_distinct(d_inner: int, d_state: int, seed: int = 0,
+                         dt_range: Tuple[float, float] = (1e-2, 1.0)) -> dict:
+    """Per-channel parameters for parity tests, every channel's rows drawn on their own, so
+    that reading another channel's parameters changes the result:
+      A[c, n] = -10^U(-2, 2), independent per (channel, state): magnitudes over four decades
+              in no order along n or c;
+      Dskip[c] in [0.25, 2], conv_b[c] in [-0.6, 0.6], each well apart from the previous
+              channel's value and from channel 0's (_separated);
+      dt_bias and conv_w as in make_params (already per channel), with steps dt0 in
+              [1e-2, 1] so that the state, and with it A, weighs in the output at bf16
+              tolerance.
+    The workloads' own distributions (make_params) give every channel the same A row, unit
+    D-skip and zero conv bias; those stay the benchmark's inputs."""
+    p = make_params(d_inner, d_state, seed=seed, dt_range=dt_range)
+    D, N = d_inner, d_state
+    g = rng(seed, "distinct")
+    A = -np.power(10.0, g.uniform(-2.0, 2.0, size=(D, N)))
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    p["A"] = f(A)
+    p["Dskip"] = f(_separated(g, D, 0.25, 2.0))
+    p["conv_b"] = f(_separated(g, D, -0.6, 0.6))
+    return p
+
+
 def make_sequence(batch: int, seqlen: int, d_inner: int, d_state: int, io: str = "bf16",
                   seed: int = 0, stream="prefill", dt_std: float = 0.5) -> dict:
     """x, dt, z [B, D, L] and Bm, Cm [B, L, N] as host torch tensors of the io dtype."""

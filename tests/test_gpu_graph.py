@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("B,D", [(1, 2048), (3, 70)])
 def test_graph_replays_match_eager(B, D):
     N, L, T = 16, 200, 8
-    prm = dev(I.make_params(D, N, seed=31))
+    prm = dev(I.make_params_distinct(D, N, seed=31))
     s = dev(I.make_sequence(B, L, D, N, "bf16", seed=31))
     toks = [dev(I.make_decode_token(B, D, N, t, "bf16", seed=31)) for t in range(T)]
     h = torch.empty(B, D, N, device=DEV)
@@ -60,7 +60,7 @@ def test_prefill_graph_replays_match_eager(N, hint):
     """A captured prefill (windowed and one-lane forms) replayed on new inputs copied into its
     static buffers: each replay equals an eager prefill of those inputs, bit for bit."""
     B, L, D = 2, 777, 96
-    prm = dev(I.make_params(D, N, seed=33))
+    prm = dev(I.make_params_distinct(D, N, seed=33))
     sets = [dev(I.make_sequence(B, L, D, N, "bf16", seed=33 + k)) for k in range(3)]
     refs = []
     for s in sets:
@@ -103,7 +103,7 @@ def test_concurrent_host_threads_and_streams():
     import threading
 
     N, L, D, T = 16, 300, 64, 4
-    prm = dev(I.make_params(D, N, seed=35))
+    prm = dev(I.make_params_distinct(D, N, seed=35))
     work = []
     for k in range(4):
         B = 1 + k

@@ -41,7 +41,7 @@ def row_oracle(seq, prm, b, n=None, h0=None, conv0=None):
 def test_prefill_split_over_batch_rows(N):
     L = 8
     note(f"large prefill B={B} D={D} L={L} N={N}")
-    prm = I.make_params(D, N, seed=61)
+    prm = I.make_params_distinct(D, N, seed=61)
     seq = I.make_sequence_device(B, L, D, N, "bf16", seed=61, device=DEV)
     pd = dev(prm)
     y, h, c = ssm.prefill(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], pd)
@@ -61,7 +61,7 @@ def test_prefill_split_over_batch_rows(N):
 @pytest.mark.parametrize("N", [16, 4])
 def test_decode_split_over_batch_rows(N):
     note(f"large decode B={B} D={D} N={N}")
-    prm = I.make_params(D, N, seed=62)
+    prm = I.make_params_distinct(D, N, seed=62)
     g = torch.Generator(device=DEV).manual_seed(62)
     h = torch.randn(B, D, N, generator=g, device=DEV)
     c = torch.randn(B, D, 3, generator=g, device=DEV).to(torch.bfloat16).float()
@@ -83,7 +83,7 @@ def test_prefill_pool_split_over_batch_rows():
     """The pool form: each launch takes its rows' slots and lengths; the pool is shared."""
     L, N = 16, 16
     note(f"large prefill_pool B={B} D={D} L={L}")
-    prm = I.make_params(D, N, seed=64)
+    prm = I.make_params_distinct(D, N, seed=64)
     seq = I.make_sequence_device(B, L, D, N, "bf16", seed=64, device=DEV)
     g = torch.Generator().manual_seed(64)
     S = B + 3
@@ -109,7 +109,7 @@ def test_conv_front_past_the_grid_cap():
     """2^31 + 2^16 tokens in 8-token lanes: more lanes than 2^20 workgroups of 256 hold."""
     Bc, Dc, Lc = 1, 4096, (1 << 19) + 16
     note(f"large conv_silu B={Bc} D={Dc} L={Lc}")
-    prm = I.make_params(Dc, 16, seed=65)
+    prm = I.make_params_distinct(Dc, 16, seed=65)
     x = I.make_sequence_device(Bc, Lc, Dc, 1, "bf16", seed=65, device=DEV)["x"]
     u = ssm.conv_silu(x, dev(prm))
     torch.cuda.synchronize()
@@ -148,7 +148,7 @@ def _decode_rows_case(Bn, Dn, check, seed):
     large, odd divisors through it, on both sides of a launch split."""
     N = 16
     note(f"decode rows B={Bn} D={Dn} (launch split every {(1 << 31) // (64 * (Dn + 16))} rows)")
-    prm = I.make_params(Dn, N, seed=seed)
+    prm = I.make_params_distinct(Dn, N, seed=seed)
     g = torch.Generator(device=DEV).manual_seed(seed)
     bf = torch.bfloat16
     tok = {"x": torch.randn(Bn, Dn, generator=g, device=DEV).to(bf),

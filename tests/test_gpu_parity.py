@@ -6,6 +6,7 @@ import torch
 import oracle
 import selective_state_space_causal_amd as ssm
 from selective_state_space_causal_amd import inputs as I
+from tests import parity_cases as PC
 from tests.gpu_common import DEV, TAU, assert_bitwise, assert_close, dev, f64, note, sample_pairs, threads
 
 pytestmark = pytest.mark.gpu
@@ -35,30 +36,23 @@ def test_tiny_fp32_workload():
     note(f"tiny max err y {ey:.2e} h {eh:.2e}")
 
 
-def test_mamba130m_workload_full_tensors():
+@pytest.mark.parametrize("params", ["workload", "distinct"])
+def test_mamba130m_workload_full_tensors(params):
+    """The workload's own parameter distributions, and per-channel ones (make_params_distinct)
+    on the same inputs; it runs the 12-channel workgroup shape, with a ragged last group."""
     w = I.WORKLOADS["mamba130m"]
-    note(f"mamba130m: B={w.batch} L={w.seqlen} D={w.d_inner} N={w.d_state} {w.io}")
-    prm = I.make_params(w.d_inner, w.d_state)
+    note(f"mamba130m ({params} params): B={w.batch} L={w.seqlen} D={w.d_inner} N={w.d_state} {w.io}")
+    mk = I.make_params if params == "workload" else I.make_params_distinct
+    prm = mk(w.d_inner, w.d_state)
     seq = I.make_sequence(w.batch, w.seqlen, w.d_inner, w.d_state, w.io)
     ey, eh = check_full(seq, prm, w.io, what="mamba130m")
     note(f"mamba130m max err y {ey:.2e} h {eh:.2e}")
 
 
-EDGE = [
-    # B, L, D, N, io, gate, conv_b
-    (1, 1, 1, 1, "f32", True, True), (1, 2, 3, 4, "f32", False, True), (2, 3, 5, 16, "bf16", True, False),
-    (3, 4, 65, 16, "bf16", True, True), (1, 5, 64, 15, "f32", True, True), (2, 63, 130, 16, "bf16", False, True),
-    (1, 64, 7, 8, "f32", True, False), (2, 65, 64, 16, "bf16", True, True), (1, 127, 33, 16, "f32", True, True),
-    (1, 513, 3, 16, "bf16", True, True), (1, 1000, 66, 3, "f32", True, True), (3, 777, 129, 16, "bf16", True, True),
-]
-
-
-@pytest.mark.parametrize("B,L,D,N,io,gate,cb", EDGE)
+@pytest.mark.parametrize("B,L,D,N,io,gate,cb", PC.EDGE)
 def test_edge_shapes(B, L, D, N, io, gate, cb):
     note(f"edge B={B} L={L} D={D} N={N} {io} gate={gate} conv_b={cb}")
-    prm = I.make_params(D, N, seed=L + D)
-    prm["conv_b"] = prm["conv_b"] + 0.1 if cb else None
-    seq = I.make_sequence(B, L, D, N, io, seed=B + 7 * L)
+    prm, seq = PC.edge_inputs(B, L, D, N, io, gate, cb)
     check_full(seq, prm, io, gate, what=f"edge{B},{L},{D},{N}")
 
 
@@ -67,7 +61,7 @@ def test_chunked_prefill_from_cache(io):
     """prefill(L1) then prefill(L2) resumed from its cache == prefill(L1 + L2)."""
     B, D, N, L1, L2 = 2, 70, 16, 300, 211
     note(f"chunked prefill {io}")
-    prm = I.make_params(D, N, seed=3)
+    prm = I.make_params_distinct(D, N, seed=3)
     seq = I.make_sequence(B, L1 + L2, D, N, io, seed=3)
     part = lambda s, a, b: {k: (v[:, :, a:b] if k in ("x", "dt", "z") else v[:, a:b]).contiguous()
                             for k, v in s.items()}
@@ -81,18 +75,15 @@ def test_chunked_prefill_from_cache(io):
     assert_bitwise(c2, cr, "chunked conv")
 
 
-@pytest.mark.parametrize("io,B,D,N", [("f32", 2, 40, 16), ("bf16", 3, 130, 16), ("bf16", 1, 5, 3)])
+@pytest.mark.parametrize("io,B,D,N", PC.DECODE)
 def test_decode_steps_match_oracle(io, B, D, N):
     """Prefill, then T single-token steps from the cache; y, h each step, conv bitwise each step."""
-    L, T = 97, 24
     note(f"decode {io} B={B} D={D} N={N}")
-    prm = I.make_params(D, N, seed=5)
-    seq = I.make_sequence(B, L, D, N, io, seed=5)
+    prm, seq, toks = PC.decode_inputs(io, B, D, N)
     _, h, c = run(seq, prm)
     _, hr, cr = oracle.prefill(seq, prm)
     pd = dev(prm)
-    for t in range(T):
-        tok = I.make_decode_token(B, D, N, t, io, seed=5)
+    for t, tok in enumerate(toks):
         td = dev(tok)
         y = ssm.decode_step(td["x"], td["dt"], td["z"], td["Bm"], td["Cm"], pd, h, c)
         yr, hr, cr = oracle.decode_step(tok, prm, hr, cr)
@@ -104,7 +95,7 @@ def test_decode_steps_match_oracle(io, B, D, N):
 def test_decode_equals_longer_prefill():
     """State caching invariant on the GPU: prefill(L1) + L2 decode steps == prefill(L1 + L2)."""
     B, D, N, L1, L2 = 2, 96, 16, 200, 40
-    prm = I.make_params(D, N, seed=9)
+    prm = I.make_params_distinct(D, N, seed=9)
     seq = I.make_sequence(B, L1 + L2, D, N, "bf16", seed=9)
     yf, hf, cf = run(seq, prm)
     s = dev(seq)
@@ -124,7 +115,7 @@ def test_channel_and_batch_slices_are_bitwise():
     """Channel locality on the GPU: a channel slice (or batch row) run alone reproduces the
     full run bit for bit when the decomposition is pinned with chunk_hint."""
     B, L, D, N = 3, 300, 200, 16
-    prm = I.make_params(D, N, seed=11)
+    prm = I.make_params_distinct(D, N, seed=11)
     seq = I.make_sequence(B, L, D, N, "bf16", seed=11)
     y, h, c = run(seq, prm, chunk_hint=1)
     for lo, hi in ((0, 64), (64, 65), (65, 200)):
@@ -140,7 +131,9 @@ def test_channel_and_batch_slices_are_bitwise():
 
 
 def test_pow2_scaling_bitwise():
-    """Dskip = 0: doubling C doubles y; doubling B doubles h and y (exact in binary fp)."""
+    """Dskip = 0: doubling C doubles y; doubling B doubles h and y (exact in binary fp).  The
+    workload's parameters keep every decay well above the fp32 subnormal range, where a doubled
+    product could escape a flush to zero that the plain one takes."""
     B, L, D, N = 2, 150, 70, 16
     prm = I.make_params(D, N, seed=13)
     prm["Dskip"] = torch.zeros_like(prm["Dskip"])
@@ -155,7 +148,7 @@ def test_pow2_scaling_bitwise():
 def test_deterministic_and_in_bounds():
     """Two runs are bitwise equal, and nothing is written outside the outputs (canaries)."""
     B, L, D, N = 2, 333, 97, 16
-    prm = dev(I.make_params(D, N, seed=17))
+    prm = dev(I.make_params_distinct(D, N, seed=17))
     s = dev(I.make_sequence(B, L, D, N, "bf16", seed=17))
     pad = 4096
     outs = []
@@ -179,7 +172,7 @@ def test_deterministic_and_in_bounds():
 def test_cache_roundtrip_through_host():
     """Copying the cache to the host and back, then resuming, equals resuming directly."""
     B, L, D, N = 1, 100, 64, 16
-    prm = dev(I.make_params(D, N, seed=19))
+    prm = dev(I.make_params_distinct(D, N, seed=19))
     s = dev(I.make_sequence(B, L, D, N, "bf16", seed=19))
     _, h, c = ssm.prefill(s["x"], s["dt"], s["z"], s["Bm"], s["Cm"], prm)
     h2, c2 = h.cpu().to(DEV), c.cpu().to(DEV)
@@ -218,28 +211,19 @@ def test_error_paths_with_real_tensors():
                         y_t=torch.empty(B, D // 2, dtype=torch.bfloat16, device=DEV))
 
 
-WINDOWED = [
-    # B, L, D, io: aligned and ragged lengths, single-lane and single-window sequences,
-    # channel counts that leave idle waves in the last workgroup
-    (1, 8, 8, "bf16"), (1, 512, 16, "bf16"), (2, 520, 13, "bf16"), (1, 1024, 9, "f32"), (1, 4104, 24, "bf16"),
-    (3, 1536, 17, "f32"), (1, 2000, 8, "bf16"), (2, 7, 3, "f32"), (1, 1030, 31, "bf16"),
-]
-
-
-@pytest.mark.parametrize("B,L,D,io", WINDOWED)
+@pytest.mark.parametrize("B,L,D,io", PC.WINDOWED)
 def test_windowed_kernel_shapes(B, L, D, io):
-    """The windowed (lanes over time) prefill, forced with chunk_hint=8, against the oracle."""
+    """The windowed (lanes over time) prefill, forced with chunk_hint=8, against the oracle:
+    fresh, then without a gate resumed from a random cache."""
     note(f"windowed B={B} L={L} D={D} {io}")
-    prm = I.make_params(D, 16, seed=L)
-    seq = I.make_sequence(B, L, D, 16, io, seed=L + 1)
+    prm, seq = PC.windowed_inputs(B, L, D, io)
     check_full(seq, prm, io, what=f"windowed{B},{L},{D}", chunk_hint=8)
-    prm2 = dict(prm, conv_b=prm["conv_b"] - 0.05)
     s = dev(seq)
-    h0 = torch.randn(B, D, 16, device=DEV)
-    c0 = torch.randn(B, D, 3, device=DEV)
-    y, h, c = ssm.prefill(s["x"], s["dt"], None, s["Bm"], s["Cm"], dev(prm2), h0=h0, conv0=c0, chunk_hint=8)
-    yr, hr, cr = oracle.scan(seq["x"], seq["dt"], None, seq["Bm"], seq["Cm"], prm2["A"], prm2["Dskip"],
-                             prm2["dt_bias"], prm2["conv_w"], prm2["conv_b"], h0=f64(h0), conv0=f64(c0))
+    h0, c0 = PC.random_cache(B, D, 16, seed=L, io=io)
+    y, h, c = ssm.prefill(s["x"], s["dt"], None, s["Bm"], s["Cm"], dev(prm), h0=h0.to(DEV), conv0=c0.to(DEV),
+                          chunk_hint=8)
+    yr, hr, cr = oracle.scan(seq["x"], seq["dt"], None, seq["Bm"], seq["Cm"], prm["A"], prm["Dskip"],
+                             prm["dt_bias"], prm["conv_w"], prm["conv_b"], h0=f64(h0), conv0=f64(c0))
     assert_close(y, yr, TAU[io], "windowed resumed y")
     assert_close(h, hr, TAU[io], "windowed resumed h")
     assert_bitwise(c, cr, "windowed resumed conv")
@@ -247,7 +231,7 @@ def test_windowed_kernel_shapes(B, L, D, io):
 
 def test_windowed_and_sequential_agree():
     B, L, D, N = 2, 3000, 40, 16
-    prm = I.make_params(D, N, seed=21)
+    prm = I.make_params_distinct(D, N, seed=21)
     seq = I.make_sequence(B, L, D, N, "f32", seed=21)
     ya, ha, ca = run(seq, prm, chunk_hint=8)
     yb, hb, cb = run(seq, prm, chunk_hint=1)
@@ -262,7 +246,7 @@ def test_bf16_output_is_rne_of_fp32_output(L, D):
     identical, so the bf16 outputs must be the round-to-nearest-even of the fp32 outputs (bit for
     bit) and the fp32 state identical -- for prefill and for a decode step."""
     B, N = 2, 16
-    prm = dev(I.make_params(D, N, seed=41))
+    prm = dev(I.make_params_distinct(D, N, seed=41))
     s16 = dev(I.make_sequence(B, L, D, N, "bf16", seed=41))
     s32 = {k: v.float() for k, v in s16.items()}
     y16, h16, c16 = ssm.prefill(s16["x"], s16["dt"], s16["z"], s16["Bm"], s16["Cm"], prm)
@@ -284,10 +268,13 @@ def test_launch_shapes_agree_bitwise():
     the same, so every run must give the same bits (the channel-slice invariant, across launch
     shapes).  On a 256-CU MI355X: all 4 rows of 3990 channels and one row alone run 16 channels
     per workgroup; a 2990-channel slice runs 12; a 1995-channel slice runs 8 (each with a
-    ragged last workgroup)."""
+    ragged last workgroup).  With per-channel parameters, the channels at the edges of the
+    workgroups, the ragged last group of each shape among them, are also checked against the
+    oracle."""
     B, L, D, N = 4, 1040, 3990, 16
     note(f"launch shapes: B={B} L={L} D={D}")
-    prm = dev(I.make_params(D, N, seed=51))
+    prm_h = I.make_params_distinct(D, N, seed=51)
+    prm = dev(prm_h)
     seq = I.make_sequence_device(B, L, D, N, "bf16", seed=51, device=DEV)
     y, h, c = ssm.prefill(seq["x"], seq["dt"], seq["z"], seq["Bm"], seq["Cm"], prm)
     for b in range(B):
@@ -298,44 +285,24 @@ def test_launch_shapes_agree_bitwise():
             torch.cuda.synchronize()
             assert torch.equal(yb[0].view(torch.int16), y[b, :n].view(torch.int16)), (b, n)
             assert torch.equal(hb[0], h[b, :n]) and torch.equal(cb[0], c[b, :n]), (b, n)
+    edges = {0, 1, 7, 8, 11, 12, 15, 16, 1991, 1992, 1993, 1994, 2987, 2988, 2989, 3983, 3984, 3989}
+    rnd = np.random.default_rng(51).integers(0, D, 8)
+    pairs = [(b, int(ch)) for b in (0, B - 1) for ch in sorted(edges | set(rnd.tolist()))]
+    for (b, ch), (yr, hr, cr) in zip(pairs, oracle.scan_channels(seq, prm_h, pairs)):
+        assert_close(y[b, ch], yr, TAU["bf16"], f"shapes y[{b},{ch}]")
+        assert_close(h[b, ch], hr, TAU["bf16"], f"shapes h[{b},{ch}]")
+        assert_bitwise(c[b, ch], cr, f"shapes conv[{b},{ch}]")
 
 
-# The method's degenerate regimes, each against the oracle through both prefill decompositions
-# and a few decode steps:
-#   a_near_zero  A = -1e-12: exp(delta A) rounds to 1 in fp32, so the state is a running sum;
-#   a_huge       A = -1e6: exp(delta A) underflows to 0, so each token's state forgets the past;
-#   a_mixed      A[c, n] from -1e-12 to -1e6 across the states of a channel;
-#   dt_tiny      dt = -60: delta = softplus(...) ~ 1e-28, the step is nearly the identity;
-#   dt_huge      dt = +60: delta ~ 55-60, large steps with full decay;
-#   x_zero       x = 0 with a conv bias: u is the same constant at every token.
-REGIMES = ["a_near_zero", "a_huge", "a_mixed", "dt_tiny", "dt_huge", "x_zero"]
-
-
-def _regime(name, prm, seq):
-    prm, seq = dict(prm), dict(seq)
-    D, N = prm["A"].shape
-    if name == "a_near_zero":
-        prm["A"] = torch.full((D, N), -1e-12, dtype=torch.float32)
-    elif name == "a_huge":
-        prm["A"] = torch.full((D, N), -1e6, dtype=torch.float32)
-    elif name == "a_mixed":
-        mags = torch.logspace(-12, 6, N, dtype=torch.float64).to(torch.float32)
-        prm["A"] = (-mags).repeat(D, 1).contiguous()
-    elif name in ("dt_tiny", "dt_huge"):
-        seq["dt"] = torch.full_like(seq["dt"], -60.0 if name == "dt_tiny" else 60.0)
-    elif name == "x_zero":
-        seq["x"] = torch.zeros_like(seq["x"])
-        prm["conv_b"] = torch.full((D,), 0.3, dtype=torch.float32)
-    return prm, seq
-
-
+# The method's degenerate regimes (tests/parity_cases.py), each against the oracle through both
+# prefill decompositions and a few decode steps.
 @pytest.mark.parametrize("chunk_hint", [0, 1])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("regime", REGIMES)
+@pytest.mark.parametrize("regime", PC.REGIMES)
 def test_degenerate_regimes(regime, io, chunk_hint):
     B, L, D, N, T = 2, 600, 24, 16, 3  # L: one full 512-token window and a ragged one
     note(f"regime {regime} {io} chunk_hint={chunk_hint}")
-    prm, seq = _regime(regime, I.make_params(D, N, seed=17), I.make_sequence(B, L, D, N, io, seed=17))
+    prm, seq = PC.regime(regime, PC.regime_params(D, N), I.make_sequence(B, L, D, N, io, seed=17))
     y, h, c = run(seq, prm, chunk_hint=chunk_hint)
     torch.cuda.synchronize()
     yr, hr, cr = oracle.prefill(seq, prm, nthreads=threads())
@@ -344,7 +311,7 @@ def test_degenerate_regimes(regime, io, chunk_hint):
     assert_bitwise(c, cr, f"{regime} conv")
     pd = dev(prm)
     for t in range(T):
-        _, tok = _regime(regime, prm, I.make_decode_token(B, D, N, t, io, seed=17))
+        _, tok = PC.regime(regime, prm, I.make_decode_token(B, D, N, t, io, seed=17))
         td = dev(tok)
         yt = ssm.decode_step(td["x"], td["dt"], td["z"], td["Bm"], td["Cm"], pd, h, c)
         yrt, hr, cr = oracle.decode_step(tok, prm, hr, cr)

@@ -7,6 +7,7 @@ import torch
 import oracle
 import selective_state_space_causal_amd as ssm
 from selective_state_space_causal_amd import inputs as I
+from tests import parity_cases as PC
 from tests.gpu_common import DEV, TAU, assert_bitwise, assert_close, dev, f64, note
 
 pytestmark = pytest.mark.gpu
@@ -29,15 +30,9 @@ def row_oracle(seq, prm, b, n, h0=None, conv0=None):
     return y[0], h[0], c[0]
 
 
-@pytest.mark.parametrize("L,N,io,hint", [(704, 16, "bf16", 0), (701, 16, "bf16", 0), (600, 16, "f32", 0),
-                                         (300, 8, "bf16", 0), (704, 16, "bf16", 1)])
-def test_prefill_pool_ragged_lengths_and_slots(L, N, io, hint):
-    B, D, S = 5, 40, 7
-    note(f"prefill_pool L={L} N={N} {io} hint={hint}")
-    prm = I.make_params(D, N, seed=51)
-    seq = I.make_sequence(B, L, D, N, io, seed=51)
-    lens = [L, 1, 333, 0, L - 5]
-    slots = [5, 2, -1, 0, 6]
+def run_pool_case(L, N, io, hint, seq, prm):
+    B, D, S = PC.POOL_B, PC.POOL_D, PC.POOL_S
+    lens, slots = PC.POOL_LENS(L), PC.POOL_SLOTS
     s = dev(seq)
     y = torch.full((B, D, L), SENT_Y, dtype=seq["x"].dtype, device=DEV)
     hp = torch.full((S, D, N), SENT_H, device=DEV)
@@ -60,12 +55,38 @@ def test_prefill_pool_ragged_lengths_and_slots(L, N, io, hint):
         assert np.all(hh[e] == SENT_H) and np.all(ch[e] == SENT_C), f"pool entry {e} must stay untouched"
 
 
+@pytest.mark.parametrize("L,N,io,hint", PC.POOL)
+def test_prefill_pool_ragged_lengths_and_slots(L, N, io, hint):
+    note(f"prefill_pool L={L} N={N} {io} hint={hint}")
+    prm, seq = PC.pool_inputs(L, N, io)
+    run_pool_case(L, N, io, hint, seq, prm)
+
+
+@pytest.mark.parametrize("L,N,io,hint", [(704, 16, "bf16", 0), (701, 16, "bf16", 0), (600, 16, "f32", 0),
+                                         (704, 16, "bf16", 1), (300, 8, "bf16", 0)])
+def test_prefill_pool_ignores_what_lies_past_a_row(L, N, io, hint):
+    """The tensors of a ragged batch hold whatever the caller left past each row's length
+    (stale tokens, padding).  Filled there with NaN and +-Inf in x, dt, z, B and C, every row's
+    outputs, state and conv window must still match the oracle run on that row's own tokens:
+    the windowed kernel's last window covers tokens past the end and must not let them into
+    the state."""
+    note(f"prefill_pool poisoned padding L={L} N={N} {io} hint={hint}")
+    prm, seq = PC.pool_inputs(L, N, io)
+    bad = torch.tensor([float("nan"), float("inf"), -float("inf")])
+    poisoned = {k: v.clone() for k, v in seq.items()}
+    for b, n in enumerate(PC.POOL_LENS(L)):
+        for k, v in poisoned.items():
+            tail = v[b, :, n:] if k in ("x", "dt", "z") else v[b, n:]
+            tail.copy_(bad[torch.arange(tail.numel()) % 3].reshape(tail.shape).to(v.dtype))
+    run_pool_case(L, N, io, hint, poisoned, prm)
+
+
 @pytest.mark.parametrize("N", [16, 4])
 def test_chunked_prefill_and_decode_through_pool(N):
     """Two prefill chunks (the second resumed from the pool) with ragged lengths, then decode steps
     with a permuted slot map: every row against the oracle run on its own tokens."""
     B, D, S, L1, L2, T = 3, 36, 5, 256, 200, 6
-    prm = I.make_params(D, N, seed=53)
+    prm = I.make_params_distinct(D, N, seed=53)
     s1 = I.make_sequence(B, L1, D, N, "bf16", seed=53)
     s2 = I.make_sequence(B, L2, D, N, "bf16", seed=54)
     n1, n2 = [256, 100, 17], [200, 3, 150]
@@ -105,7 +126,7 @@ def test_chunked_prefill_and_decode_through_pool(N):
 
 def test_decode_pool_with_identity_slots_equals_decode():
     B, D, N = 4, 96, 16
-    prm = dev(I.make_params(D, N, seed=57))
+    prm = dev(I.make_params_distinct(D, N, seed=57))
     h = torch.randn(B, D, N, device=DEV)
     c = torch.randn(B, D, 3, device=DEV)
     h2, c2 = h.clone(), c.clone()

@@ -78,7 +78,7 @@ def test_projection_errors(pj):
 @pytest.mark.parametrize("resume", [False, True])
 def test_conv_silu_matches_oracle(io, B, D, Ls, resume):
     note(f"conv_silu io={io} B={B} D={D} L={Ls} resume={resume}")
-    prm = I.make_params(D, 16)
+    prm = I.make_params_distinct(D, 16)
     g = torch.Generator().manual_seed(B * 100 + D * 10 + Ls)
     x = torch.randn(B, D, Ls, generator=g).to(DT[io])
     conv0 = torch.randn(B, D, 3, generator=g).to(DT[io]).float() if resume else None
@@ -94,7 +94,7 @@ def test_conv_silu_matches_oracle(io, B, D, Ls, resume):
 def test_conv_silu_resume_is_bitwise():
     """Running tokens [L1, L) with the last three raw inputs before L1 as history reproduces
     the tail of the full run bit for bit (the arithmetic per token is the same)."""
-    prm = {k: v.to(DEV) for k, v in I.make_params(12, 16).items() if v is not None}
+    prm = {k: v.to(DEV) for k, v in I.make_params_distinct(12, 16).items() if v is not None}
     x = torch.randn(2, 12, 96, device=DEV).to(torch.bfloat16)
     full = L.conv_silu(x, prm)
     for L1 in (8, 40, 88):
@@ -112,7 +112,7 @@ def test_layer_small_matches_oracle(pj, rows, out_f32, fused):
     as conv_silu then three GEMMs.  The out partial in bf16 (default) or fp32."""
     w8 = I.LAYERS["layer_small"]
     note(f"layer {w8} rows={rows} out_f32={out_f32}")
-    prm = I.make_params(w8.d_inner, w8.d_state)
+    prm = I.make_params_distinct(w8.d_inner, w8.d_state)
     wts = I.make_proj_weights(w8.d_model, w8.d_inner, w8.dt_rank, w8.d_state, w8.io)
     hidden = I.make_hidden(w8.batch, w8.seqlen, w8.d_model, w8.io)[:rows].contiguous()
     wd = {k: v.to(DEV) for k, v in wts.items() if k not in ("in_x", "in_z")}
@@ -192,8 +192,7 @@ def test_conv_xproj_matches_oracle(B, Ls, D, R, N, resume):
     rounding the fp32 front end may take the other way (one ulp each, found from the fp64
     values), and the final bf16 rounding."""
     note(f"conv_xproj B={B} L={Ls} D={D} R={R} N={N} resume={resume}")
-    prm = I.make_params(D, 16, seed=D + R)
-    prm["conv_b"] = prm["conv_b"] + 0.05
+    prm = I.make_params_distinct(D, 16, seed=D + R)
     g = torch.Generator().manual_seed(B * 1000 + Ls + D + R)
     x = torch.randn(B, D, Ls, generator=g).to(torch.bfloat16)
     w = (torch.randn(R + 2 * N, D, generator=g) / D ** 0.5).to(torch.bfloat16)
@@ -236,7 +235,7 @@ def test_conv_xproj_full_size_sampled():
     dot products, with the bound of test_conv_xproj_matches_oracle."""
     w8 = I.LAYERS["layer7b"]
     D, Ls, R, N = w8.d_inner, w8.seqlen, w8.dt_rank, w8.d_state
-    prm = I.make_params(D, N)
+    prm = I.make_params_distinct(D, N)
     pd = {k: v.to(DEV) for k, v in prm.items() if v is not None}
     wall = I.make_proj_weights(w8.d_model, D, R, N, w8.io, device=DEV)["x_all"]
     x = I.make_sequence_device(1, Ls, D, 1, "bf16", device=DEV)["x"]
