@@ -162,6 +162,9 @@ def traffic_from_profiles(workload, kernel=None):
 PMC_COMMAND = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} -d $REPO/gpurun_out/pmc -o {ctr} "
                "--output-format csv -- python3 $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline "
                "--decode-steps 8 --copy-calibration --workload {workload}")
+PMC_COMMAND_DECODE = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} -d $REPO/gpurun_out/pmc_{scale} -o {ctr} "
+                      "--output-format csv -- python3 $REPO/bench.py --decode-at-scale-only {scale} --steps 2 "
+                      "--warmup 1")
 PMC_COMMAND_CODEC = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} -d $REPO/gpurun_out/pmc_codec -o {ctr} "
                      "--output-format csv -- python3 $REPO/bench.py --codec {workload} --steps 2 --warmup 1 "
                      "--no-cpu-baseline --copy-calibration")
@@ -219,8 +222,8 @@ def record_issue(csv_path, workload):
 
 
 def issue_from_profiles(workload):
-    """The prefill kernel's recorded VALU issue occupancy, or None (no record, or the kernel
-    sources changed since it was taken)."""
+    """The prefill kernel's recorded VALU issue counters (record_issue), or None (no record, or
+    the kernel sources changed since they were taken)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -230,7 +233,69 @@ def issue_from_profiles(workload):
         return None
     if not rec or rec.get("source_hash") != kernel_source_hash("scan"):
         return None
-    return rec.get("valu_issue_busy")
+    return rec
+
+
+def calib_from_profiles():
+    """The committed rate calibration (profiles/calib.json, written by
+    python -m selective_state_space_causal_amd.calib), or None when it is missing or its
+    microbenchmarks changed since it was taken."""
+    from selective_state_space_causal_amd import calib
+
+    path = os.path.join(ROOT, "profiles", "calib.json")
+    try:
+        rec = json.load(open(path))
+    except (ValueError, OSError):
+        return None
+    return rec if rec.get("source_hash") == calib.source_hash() else None
+
+
+# The vector ALUs of an MI355X (AMD public specification): 256 CUs of 4 SIMDs, each SIMD 16
+# lanes wide, at 2.4 GHz; a wave64 VALU instruction is issued to its SIMD in a 4-cycle slot.
+# How many instructions a SIMD completes per slot depends on the instruction and on the waves
+# it holds, and is measured (selective_state_space_causal_amd.calib): at two waves per SIMD,
+# plain fp32 arithmetic reaches ~1.5 per slot (two waves issue in the same slot) and v_exp_f32
+# ~0.47 (a transcendental holds the SIMD for two slots and is not paired).
+MI355X_CUS, SIMDS_PER_CU, SIMD_LANES, CLOCK_HZ = 256, 4, 16, 2.4e9
+SLOTS_PER_S = MI355X_CUS * SIMDS_PER_CU * CLOCK_HZ / 4  # per SIMD-slot, chip-wide
+
+
+def valu_roofline(issue, cal, kernel_ms):
+    """Issue roofline of the prefill kernel (bound "alu").  From the committed counters, per
+    wave: SQ_INSTS_VALU = plain + transcendental instructions and SQ_ACTIVE_INST_VALU = plain +
+    2 x transcendental slots, so trans = active - insts and plain = insts - trans.  The kernel's
+    shortest possible duration at the calibrated rates (plain at the fp32 FMA rate, trans at the
+    v_exp_f32 rate, both per SIMD per slot at the kernel's waves per SIMD) is
+        t_min = waves x (plain / R_plain + trans / R_trans) / (1024 SIMDs x 0.6e9 slots/s),
+    the rates' slots taken at the published 2.4 GHz.  achieved = all VALU lane-operations /
+    the measured kernel time; peak = the same operations / t_min; frac = t_min / time.  DPP
+    instructions count as plain although they do not pair (measured ~0.9 per slot), so the
+    peak is on the high side.  Null where the counters or the calibration are stale or
+    missing."""
+    out = {"bound": "alu", "unit": "T lane-ops/s", "achieved": None, "peak": None, "frac": None,
+           "valu_insts_per_wave": None, "trans_per_wave": None, "waves_per_simd": None,
+           "rates_inst_per_slot": None, "valu_issue_busy": None}
+    if issue is None:
+        return out
+    from selective_state_space_causal_amd import calib
+
+    waves = issue["waves"]
+    wps = waves / (MI355X_CUS * SIMDS_PER_CU)
+    insts = issue["insts_valu_per_wave"]
+    trans = issue["active_inst_valu_per_wave"] - insts
+    plain = insts - trans
+    lane_ops = waves * insts * 64
+    out.update({"achieved": round(lane_ops / (kernel_ms * 1e-3) / 1e12, 3), "valu_insts_per_wave": insts,
+                "trans_per_wave": round(trans, 1), "waves_per_simd": round(wps, 3),
+                "valu_issue_busy": issue.get("valu_issue_busy")})
+    if cal is not None:
+        w = max(1, round(wps))
+        rp, rt = calib.rate(cal, "fma", w), calib.rate(cal, "exp", w)
+        t_min = waves * (plain / rp + trans / rt) / SLOTS_PER_S
+        out.update({"rates_inst_per_slot": {"plain": rp, "trans": rt, "at_waves_per_simd": w},
+                    "t_min_ms": round(t_min * 1e3, 4), "peak": round(lane_ops / t_min / 1e12, 3),
+                    "frac": round(t_min / (kernel_ms * 1e-3), 4)})
+    return out
 
 
 def record_traffic(pmc_dir, workload):
@@ -270,7 +335,10 @@ def record_traffic(pmc_dir, workload):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     codec = kernel("q8_") is not None
-    cmd = (PMC_COMMAND_CODEC if codec else PMC_COMMAND).format(ctr="<FETCH_SIZE|WRITE_SIZE>", workload=workload)
+    if workload.startswith("decode_"):  # decode_warm / decode_hbm: the --decode-at-scale-only runs
+        cmd = PMC_COMMAND_DECODE.format(ctr="<FETCH_SIZE|WRITE_SIZE>", scale=workload[len("decode_"):])
+    else:
+        cmd = (PMC_COMMAND_CODEC if codec else PMC_COMMAND).format(ctr="<FETCH_SIZE|WRITE_SIZE>", workload=workload)
     group = "codec" if codec else "scan"
     entry = {"sources": group, "source_hash": kernel_source_hash(group), "command": cmd,
              "copy_calibration": {"kernel": copy_name, "fetch_scale": round(fetch_scale, 4),
@@ -514,19 +582,48 @@ def layer_cpu_baseline(w, hidden, wts, prm, tokens):
                       f"C fp64 scan over {cores} threads", "seconds": round(dt, 3)}
 
 
-def decode_at_scale(args, copy_gbps):
-    """The decode step where it moves enough bytes to be bound by HBM rather than by launch
-    latency: the mamba2.8b cache (batch 64, d_inner 5120, d_state 16: 21 MB of h, 3.9 MB of
-    conv window), left by a 64-token prefill of that shape, then its 256 decode steps on their
-    own seeded tokens, replayed from one captured HIP graph per step sequence as a serving loop
-    runs them.  Inputs resident in HBM before timing; HIP events around each replay."""
+def plain_copy_gbps():
+    """Context for the HBM fractions: a plain 1 GiB device copy, timed (it is also the
+    byte-counter calibration dispatch of the rocprofv3 --pmc runs)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = TimingEvent(), TimingEvent()
+    c0.record(stream)
+    dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    gbps = 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    log(f"bench: plain 1 GiB copy: {gbps:.0f} GB/s (read + write)")
+    return gbps
+
+
+# The decode step where it moves enough bytes per step to be bound by memory rather than by
+# launch latency, on two caches of the Mamba-2.8B layer shape (d_inner 5120, d_state 16):
+#   warm: batch 64, the mamba2.8b workload's cache (21 MB of h + 3.9 MB of conv window), which
+#         stays in the 256 MB last-level cache (Infinity Cache) across a replay;
+#   hbm:  batch 1024 (336 MB of h + 63 MB of conv window), larger than that cache, so that
+#         every step streams its cache from HBM.
+DECODE_SCALES = {"warm": (64, 256), "hbm": (1024, 64)}  # batch, steps per replay
+LLC_BYTES = 256 << 20
+
+
+def decode_at_scale(args, copy_gbps, scale="warm"):
+    """The decode step on a cache left by a 64-token prefill of the layer shape, then its
+    decode steps on their own seeded tokens, replayed from one captured HIP graph per step
+    sequence as a serving loop runs them.  Inputs resident in HBM before timing; HIP events
+    around each replay."""
     import torch
 
     import selective_state_space_causal_amd as ssm
     from selective_state_space_causal_amd import inputs as I
 
     w = I.WORKLOADS["mamba2.8b"]
-    B, D, N, T = w.batch, w.d_inner, w.d_state, w.decode_steps
+    B, T = DECODE_SCALES[scale]
+    D, N = w.d_inner, w.d_state
     es = 2 if w.io == "bf16" else 4
     dev = torch.device("cuda:0")
     prm = I.make_params(D, N, dt_range=w.dt_range)
@@ -566,9 +663,13 @@ def decode_at_scale(args, copy_gbps):
     us = sum(each) / len(each)
     dbytes = decode_bytes(B, D, N, es)
     gbps = dbytes / (us * 1e-6) / 1e9
-    log(f"bench: decode at scale (mamba2.8b cache, {T} steps per replay): {us:.2f} us/step, {gbps:.0f} GB/s")
+    cache_bytes = B * D * (N + CONV_W - 1) * 4
+    log(f"bench: decode at scale ({scale}: batch {B}, {cache_bytes / 2**20:.0f} MiB of cache, {T} steps per "
+        f"replay): {us:.2f} us/step, {gbps:.0f} GB/s")
     del graph
-    return {"workload": "mamba2.8b", "batch": B, "d_inner": D, "d_state": N, "steps_per_replay": T,
+    return {"workload": "mamba2.8b-shaped cache" if B != w.batch else "mamba2.8b", "batch": B, "d_inner": D,
+            "d_state": N, "steps_per_replay": T, "cache_bytes": cache_bytes,
+            "cache_resident_in_llc": cache_bytes < LLC_BYTES,
             "state_from": "64-token prefill of the same shape", "mode": "hip_graph",
             "us_per_step": round(us, 3), "us_per_step_range": [round(each[0], 3), round(each[-1], 3)],
             "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -603,6 +704,10 @@ def main():
     ap.add_argument("--layer", metavar="LAYER", default=None,
                     help="instead of the scan alone, time one rank's mixer layer (layer7b): projections, conv "
                          "front, scan, and print its own JSON line")
+    ap.add_argument("--decode-at-scale-only", choices=sorted(DECODE_SCALES), default=None,
+                    help="time only the decode step on one of the two Mamba-2.8B-shaped caches (warm: batch 64, "
+                         "inside the last-level cache; hbm: batch 1024, larger than it) and print its JSON; "
+                         "for counter runs")
     ap.add_argument("--record-traffic", metavar="PMC_DIR", default=None,
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs and exit")
     ap.add_argument("--record-issue", metavar="CSV", default=None,
@@ -622,6 +727,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.decode_at_scale_only:
+        import torch
+
+        torch.cuda.set_device(0)
+        print(json.dumps(decode_at_scale(args, plain_copy_gbps(), args.decode_at_scale_only)), flush=True)
+        return
     if args.codec:
         bench_codec(args)
         return
@@ -656,19 +767,7 @@ def main():
 
     stream = torch.cuda.current_stream()
     ev = TimingEvent
-    # Context for the HBM fractions: a plain 1 GiB device copy, timed (it is also the byte-counter
-    # calibration dispatch of --copy-calibration runs).
-    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    c0, c1 = ev(), ev()
-    c0.record(stream)
-    dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    log(f"bench: plain 1 GiB copy: {copy_gbps:.0f} GB/s (read + write)")
-    del src, dst
+    copy_gbps = plain_copy_gbps()
     scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
     elems = B * L * D
     if args.pool:
@@ -769,7 +868,6 @@ def main():
     p_gbps = pbytes / (pre_ms * 1e-3) / 1e9
     d_us = dec_ms * 1e3 / T if T else None
     d_gbps = dbytes / (d_us * 1e-6) / 1e9 if T else None
-    tflops = flops_per_element(N) * elems / (pre_ms * 1e-3) / 1e12
     traffic = traffic_from_profiles(w.name)
     log(f"bench: prefill {pre_ms:.3f} ms ({gelem:.1f} Gelem/s, {p_gbps:.0f} GB/s)" +
         (f", decode {d_us:.2f} us/step ({'graph' if graph is not None else 'eager'}; eager {eager_us:.2f} us/step)"
@@ -801,16 +899,17 @@ def main():
         "copy_gbps": round(copy_gbps, 1),
         "cache_state": "cold (1 GiB scrub before each prefill)" if args.cold else "warm",
         "cache_benefit": None if not T else round(pre_ms * 1e3 / d_us, 1),
-        "roofline": {"kernel": "prefill", "bound": "alu", "achieved": round(tflops, 3),
-                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
-                     "flops_per_element": flops_per_element(N), "traffic": traffic,
-                     "valu_issue_busy": issue_from_profiles(w.name)},
+        "roofline": dict(kernel="prefill", **valu_roofline(issue_from_profiles(w.name), calib_from_profiles(), pre_ms),
+                         traffic=traffic, hbm_frac=round(p_gbps / HBM_PEAK_GBPS, 4),
+                         flops_per_element=flops_per_element(N),
+                         fp32_tflops=round(flops_per_element(N) * elems / (pre_ms * 1e-3) / 1e12, 3)),
     }
     # With the decode measurement only (not on prefill-only workloads), not in the pool form, not
     # on mamba2.8b itself (its line is that measurement), not when the decode step count is
     # overridden (the counter runs) and not when asked not to.
     if T and not (args.pool or w.name == "mamba2.8b" or args.decode_steps is not None or args.no_decode_at_scale):
-        rec["decode_at_scale"] = decode_at_scale(args, copy_gbps)
+        rec["decode_at_scale"] = decode_at_scale(args, copy_gbps, "warm")
+        rec["decode_at_scale_hbm"] = decode_at_scale(args, copy_gbps, "hbm")
     if args.pool and not args.no_cpu_baseline:
         log("bench: the CPU baseline is defined on the full workload; skipped in the pool form")
         args.no_cpu_baseline = True

@@ -89,6 +89,14 @@ def load(path: str = LIB_PATH):
     lib.ssm_conv_xproj.restype = ctypes.c_int
     lib.ssm_conv_xproj.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params), vp, vp, vp, ctypes.c_int64,
                                    vp, vp, vp, vp]
+    lib.ssm_calib_issue.restype = ctypes.c_int
+    lib.ssm_calib_issue.argtypes = [cint, i64, ctypes.c_int32, i64, vp, vp, vp]
+    lib.ssm_calib_copy.restype = ctypes.c_int
+    lib.ssm_calib_copy.argtypes = [vp, vp, sz, vp]
+    lib.ssm_calib_read.restype = ctypes.c_int
+    lib.ssm_calib_read.argtypes = [vp, sz, vp, vp]
+    lib.ssm_calib_read_sink_floats.restype = sz
+    lib.ssm_calib_read_sink_floats.argtypes = []
     if lib.ssm_abi_version() != ABI_VERSION:
         raise ImportError(f"libssm ABI {lib.ssm_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -432,3 +440,49 @@ def conv_xproj(x, params: dict, w, rank: int, conv0=None, *, lowrank=None, Bm=No
     if st != 0:
         raise SsmError("ssm_conv_xproj", st, lib.ssm_status_str(st).decode())
     return tuple(outs)
+
+
+# ---- rate calibration (include/ssm_calib.h) ----
+
+CALIB_KINDS = {"fma": 0, "exp": 1, "mix": 2, "mul": 3, "fmac": 4, "fma3": 5, "dpp": 6, "split": 7, "mixi": 8}
+CALIB_STAMP_WORDS = 8
+CALIB_THREADS = 256
+
+
+def calib_issue(kind: int, workgroups: int, iters: int, split: int = 0, *, device="cuda", stream=None):
+    """ssm_calib_issue: returns (stamps [waves, 8] int64 on the device, sink); run on `stream`."""
+    lib = load()
+    dev = torch.device(device)
+    stamps = torch.zeros(workgroups * 4, CALIB_STAMP_WORDS, dtype=torch.int64, device=dev)
+    sink = torch.empty(workgroups * CALIB_THREADS, dtype=torch.float32, device=dev)
+    st = lib.ssm_calib_issue(kind, workgroups, iters, split, _ptr(stamps), _ptr(sink), stream_handle(stream, dev))
+    if st != 0:
+        raise SsmError("ssm_calib_issue", st, lib.ssm_status_str(st).decode())
+    return stamps, sink
+
+
+def calib_copy(src, dst, *, stream=None):
+    """ssm_calib_copy of src's bytes into dst (same byte count, both contiguous on the GPU)."""
+    lib = load()
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or not (src.is_cuda and dst.is_cuda and src.is_contiguous()
+                                                     and dst.is_contiguous()):
+        raise ValueError("calib_copy: contiguous GPU tensors of the same byte count expected")
+    st = lib.ssm_calib_copy(_ptr(src), _ptr(dst), n, stream_handle(stream, src.device))
+    if st != 0:
+        raise SsmError("ssm_calib_copy", st, lib.ssm_status_str(st).decode())
+
+
+def calib_read(src, sink=None, *, stream=None):
+    """ssm_calib_read of src's bytes; returns the sink tensor."""
+    lib = load()
+    if not (src.is_cuda and src.is_contiguous()):
+        raise ValueError("calib_read: a contiguous GPU tensor expected")
+    nsink = int(lib.ssm_calib_read_sink_floats())
+    sink = torch.empty(nsink, dtype=torch.float32, device=src.device) if sink is None else sink
+    if sink.numel() < nsink or sink.dtype != torch.float32:
+        raise ValueError(f"calib_read: sink must hold {nsink} float32")
+    st = lib.ssm_calib_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), stream_handle(stream, src.device))
+    if st != 0:
+        raise SsmError("ssm_calib_read", st, lib.ssm_status_str(st).decode())
+    return sink

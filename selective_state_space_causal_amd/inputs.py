@@ -158,13 +158,15 @@ def make_sequence_device(batch: int, seqlen: int, d_inner: int, d_state: int, io
         g = torch.Generator(device=device)
         g.manual_seed(torch_seed(seed, stream, name))
         out = torch.empty(shape, dtype=dtype, device=device)
-        # draw in row chunks to bound the fp32 temporary
+        # draw in chunks of whole batch rows, up to 2^26 values, to bound the fp32 temporary
         flat = out.view(shape[0], -1)
-        for i in range(shape[0]):
-            t = torch.randn(flat.shape[1], generator=g, device=device, dtype=torch.float32)
+        rows = max(1, (1 << 26) // max(1, flat.shape[1]))
+        for r0 in range(0, shape[0], rows):
+            r1 = min(shape[0], r0 + rows)
+            t = torch.randn(r1 - r0, flat.shape[1], generator=g, device=device, dtype=torch.float32)
             if scale != 1.0:
                 t.mul_(scale)
-            flat[i].copy_(t)
+            flat[r0:r1].copy_(t)
             del t
         return out
 

@@ -42,15 +42,34 @@ def _kind(what):
     return m.group(1) if m else "other"
 
 
-def record_margin(err, tau, kind, step=None):
+def record_margin(err, tau, kind, step=None, tight=None):
     rec = MARGINS.setdefault(_test_id(), {})
     k = rec.setdefault(kind, {"err": 0.0, "tau": tau})
     k["err"] = max(k["err"], float(err))
+    if tight is not None:
+        k["tight"] = max(k.get("tight", 0.0), float(tight))
     if step is not None:
         series = rec.setdefault("per_step", {}).setdefault(kind, [])
         while len(series) <= step:
             series.append(0.0)
         series[step] = max(series[step], float(err))
+
+
+FP32_TAU = 1e-4
+
+
+def tight_ratio(gpu, ref, tau, kind):
+    """How much of a tighter bar than tau the error uses, for bf16 io (tau 2e-2, about five
+    times the output's own rounding).  The arithmetic runs in fp32 on exactly widened inputs, so
+    h is held to the fp32 bar 1e-4 (1 + |ref|), and y to the rounding of the bf16 output (at
+    most half an ulp, 2^-8 |y|) plus twice the fp32 bar.  assert_close requires the ratio to stay
+    at or below 1, so that an accuracy regression of the fp32 arithmetic cannot hide under the
+    bf16 tolerance.  Returns max(|gpu - ref| / bar), or None where no such bar applies."""
+    if tau != TAU["bf16"] or kind not in ("y", "h"):
+        return None
+    a = np.abs(ref)
+    bar = (2.0 ** -8 * a + 2 * FP32_TAU * (1.0 + a)) if kind == "y" else FP32_TAU * (1.0 + a)
+    return float((np.abs(gpu - ref) / bar).max())
 
 
 def assert_close(gpu, ref, tau, what, step=None):
@@ -62,8 +81,11 @@ def assert_close(gpu, ref, tau, what, step=None):
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
     err = np.abs(gpu - ref) / (1.0 + np.abs(ref))
     i = np.unravel_index(err.argmax(), err.shape)
-    record_margin(err.max(), tau, _kind(what), step)
+    kind = _kind(what)
+    tight = tight_ratio(gpu, ref, tau, kind)
+    record_margin(err.max(), tau, kind, step, tight)
     assert err.max() <= tau, f"{what}: max err {err.max():.3e} > {tau:.0e} at {i}: gpu {gpu[i]!r} ref {ref[i]!r}"
+    assert tight is None or tight <= 1.0, f"{what}: error {tight:.3f} x the fp32 bar (bf16 rounding aside)"
     return float(err.max())
 
 

@@ -103,7 +103,27 @@ def test_record_issue_leaves_out_the_warmup_dispatch(sandbox):
     assert issue["wave_cycles_per_wave"] == 225_000.0
     # each of the 1024 SIMDs holds two waves: busy = 2 x active / cycles
     assert issue["valu_issue_busy"] == round(2 * 99_000.0 / 225_000.0, 4)
-    assert bench.issue_from_profiles("slice7b") == issue["valu_issue_busy"]
+    assert bench.issue_from_profiles("slice7b") == issue
+
+
+def test_valu_roofline_arithmetic():
+    """plain = insts - trans, trans = active - insts; t_min = waves x (plain / R_plain + trans /
+    R_trans) slots at 1024 SIMDs x 2.4 GHz / 4; frac = t_min / kernel time."""
+    issue = {"waves": 2048, "insts_valu_per_wave": 90_000.0, "active_inst_valu_per_wave": 100_000.0,
+             "valu_issue_busy": 0.9}
+    cal = {"issue": [{"kind": k, "waves_per_simd": w, "inst_per_slot_median": r}
+                     for k, pts in (("fma", ((1, 0.75), (2, 1.5), (4, 1.6))), ("exp", ((1, 0.44), (2, 0.5), (4, 0.5))))
+                     for w, r in pts]}
+    r = bench.valu_roofline(issue, cal, 0.5)
+    assert r["waves_per_simd"] == 2.0 and r["trans_per_wave"] == 10_000.0
+    assert r["rates_inst_per_slot"] == {"plain": 1.5, "trans": 0.5, "at_waves_per_simd": 2}
+    t_min = 2048 * (80_000 / 1.5 + 10_000 / 0.5) / (1024 * 2.4e9 / 4)
+    assert r["t_min_ms"] == round(t_min * 1e3, 4)
+    assert r["frac"] == round(t_min / 0.5e-3, 4)
+    assert r["achieved"] == round(2048 * 90_000 * 64 / 0.5e-3 / 1e12, 3)
+    assert r["peak"] == round(2048 * 90_000 * 64 / t_min / 1e12, 3)
+    assert bench.valu_roofline(None, cal, 0.5)["achieved"] is None
+    assert bench.valu_roofline(issue, None, 0.5)["frac"] is None
 
 
 def test_more_than_one_gpu_is_refused():
