@@ -557,11 +557,70 @@ def bench_layer(args):
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": gemm["mfma_frac"], "traffic": None},
         "cpu_baseline": None,
     }
+    rec["decode"] = {kind: layer_decode_timing(args, w, wts, prm, pj, bufs["h"], bufs["c"], kind == "fused")
+                     for kind in ("unfused", "fused")}
     pj.close()
     if not args.no_cpu_baseline:
         log("bench: timing the layer oracle on the host")
         rec["cpu_baseline"] = layer_cpu_baseline(w, hidden, wts, prm, tokens=1024)
     print(json.dumps(rec), flush=True)
+
+
+def layer_decode_timing(args, w, wts, prm, pj, h, c, fused, T=64):
+    """Decode through one rank's layer: T tokens per batch row from the cache the timed prefill
+    left (in_proj, the per-token stages -- separate calls, or ssm_decode_fused -- and out_proj),
+    captured in one HIP graph and replayed as a serving loop runs it; HIP events around each
+    replay.  Reported per token, with the calls per token and the bytes a token must move at
+    least (every weight of the slice once, the cache read and written, the token's io)."""
+    import torch
+
+    from selective_state_space_causal_amd import inputs as I
+    from selective_state_space_causal_amd import layer
+
+    B, DM, D, R, N = w.batch, w.d_model, w.d_inner, w.dt_rank, w.d_state
+    dev = h.device
+    hidden = I.make_hidden(B, T, DM, w.io, device=dev)
+    toks = [hidden[:, t].contiguous() for t in range(T)]
+    bufs = layer.alloc_decode_buffers(toks[0], wts, N, fused)
+    plans = [layer.decode_stages(toks[t], wts, prm, pj, h, c, bufs, fused) for t in range(T)]
+    stream = torch.cuda.current_stream()
+
+    def loop():
+        for plan in plans:
+            for _, call in plan:
+                call()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        loop()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        loop()
+    torch.cuda.synchronize()
+
+    def step(e):
+        e[0].record(stream)
+        graph.replay()
+        e[1].record(stream)
+
+    marks, _ = timed_steps(step, 2, args.warmup, args.steps)
+    each = sorted(a.elapsed_time(b) * 1e3 / T for a, b in marks)
+    us = sum(each) / len(each)
+    es = 2 if w.io == "bf16" else 4
+    weight_bytes = (2 * D * DM + (R + 2 * N) * D + D * R + DM * D) * es
+    tok_bytes = weight_bytes + B * D * ((N + CONV_W - 1) * 4 * 2 + 3 * es) + B * DM * 2 * es + D * (N + 7) * 4
+    gbps = tok_bytes / (us * 1e-6) / 1e9
+    names = [n for n, _ in plans[0]]
+    log(f"bench: layer decode ({'fused' if fused else 'separate calls'}): {us:.2f} us/token over {len(names)} calls "
+        f"({', '.join(names)}), {gbps:.0f} GB/s")
+    del graph
+    return {"us_per_token": round(us, 3), "us_per_token_range": [round(each[0], 3), round(each[-1], 3)],
+            "calls_per_token": len(names), "calls": names, "tokens_per_replay": T, "mode": "hip_graph",
+            "algorithmic_bytes_per_token": tok_bytes, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
 def layer_cpu_baseline(w, hidden, wts, prm, tokens):

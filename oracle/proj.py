@@ -105,3 +105,27 @@ def layer_prefill(hidden, w: dict, params: dict, io: str = "bf16", nthreads: int
     y = to_io(y, io)
     out = out_proj(y, w["out"])
     return (to_io(out, io) if out_io else out), h, c
+
+
+def layer_decode_step(hidden_t, w: dict, params: dict, h, conv, io: str = "bf16", out_io: bool = True):
+    """One decoded token through one rank's mixer layer, as the library composes it: in_proj
+    (x_t, z_t), the conv front from the conv cache, x_proj (low-rank step input, B_t, C_t),
+    dt_proj, the decode step of the scan (the C oracle, resumed from h and conv), and out_proj;
+    every intermediate the GPU stores in the io dtype is rounded to it at the same point.
+    hidden_t [B, d_model]; h [B, D, N]; conv [B, D, 3].  Returns (out [B, d_model] fp64,
+    y [B, D], h', conv')."""
+    from . import decode_step as scan_decode  # the fp64 C oracle of the scan
+
+    hid = _f64(hidden_t)[:, None, :]                                   # [B, 1, d_model]
+    x = to_io(in_proj(hid, w["in_x"]), io)                             # [B, D, 1]
+    z = to_io(in_proj(hid, w["in_z"]), io)
+    u = to_io(conv_silu(x, params["conv_w"], params.get("conv_b"), _f64(conv)), io)
+    lowrank = to_io(x_proj(u, w["x_dt"]), io)                          # [B, 1, R]
+    Bm = to_io(x_proj(u, w["x_B"]), io)
+    Cm = to_io(x_proj(u, w["x_C"]), io)
+    dt = to_io(dt_proj(lowrank, w["dt"]), io)                          # [B, D, 1]
+    tok = {"x": x[..., 0], "dt": dt[..., 0], "z": z[..., 0], "Bm": Bm[:, 0], "Cm": Cm[:, 0]}
+    y, h2, c2 = scan_decode(tok, {k: _f64(v) for k, v in params.items() if v is not None}, _f64(h), _f64(conv))
+    y = to_io(y, io)
+    out = out_proj(y[..., None], w["out"])[:, 0]
+    return (to_io(out, io) if out_io else out), y, h2, c2

@@ -89,6 +89,11 @@ def load(path: str = LIB_PATH):
     lib.ssm_conv_xproj.restype = ctypes.c_int
     lib.ssm_conv_xproj.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params), vp, vp, vp, ctypes.c_int64,
                                    vp, vp, vp, vp]
+    lib.ssm_decode_fused_workspace_bytes.restype = sz
+    lib.ssm_decode_fused_workspace_bytes.argtypes = [ctypes.POINTER(Dims), i64]
+    lib.ssm_decode_fused.restype = ctypes.c_int
+    lib.ssm_decode_fused.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params), vp, vp, i64] + [vp] * 5 + \
+        [vp, sz, vp]
     lib.ssm_calib_issue.restype = ctypes.c_int
     lib.ssm_calib_issue.argtypes = [cint, i64, ctypes.c_int32, i64, vp, vp, vp]
     lib.ssm_calib_copy.restype = ctypes.c_int
@@ -440,6 +445,43 @@ def conv_xproj(x, params: dict, w, rank: int, conv0=None, *, lowrank=None, Bm=No
     if st != 0:
         raise SsmError("ssm_conv_xproj", st, lib.ssm_status_str(st).decode())
     return tuple(outs)
+
+
+# ---- the fused per-token layer stages (include/ssm_layer.h) ----
+
+def decode_fused_workspace_bytes(batch: int, d_inner: int, rank: int, d_state: int = 16,
+                                 io_dtype=torch.bfloat16) -> int:
+    d = Dims(batch, 1, d_inner, d_state, CONV_W, _io_code(io_dtype), 0)
+    return int(load().ssm_decode_fused_workspace_bytes(ctypes.byref(d), rank))
+
+
+def decode_fused(x_t, z_t, params: dict, w_x, w_dt, rank: int, h, conv, *, y_t=None, workspace=None, stream=None):
+    """ssm_decode_fused: x_t, z_t [B, D] (z_t may be None), w_x [rank + 2N, D], w_dt [D, rank];
+    h [B, D, N] and conv [B, D, 3] are updated in place.  Returns y_t [B, D]."""
+    lib = load()
+    Bsz, D = x_t.shape
+    N = params["A"].shape[1]
+    dev, io = x_t.device, x_t.dtype
+    _check(x_t, "x_t", (Bsz, D), io, dev)
+    _check(z_t, "z_t", (Bsz, D), io, dev, optional=True)
+    _check(w_x, "w_x", (rank + 2 * N, D), io, dev)
+    _check(w_dt, "w_dt", (D, rank), io, dev)
+    _check(h, "h", (Bsz, D, N), torch.float32, dev)
+    _check(conv, "conv", (Bsz, D, CONV_W - 1), torch.float32, dev)
+    _check_params(params, D, N, dev)
+    y_t = torch.empty_like(x_t) if y_t is None else y_t
+    _check(y_t, "y_t", (Bsz, D), io, dev)
+    d = Dims(Bsz, 1, D, N, CONV_W, _io_code(io), 0)
+    need = int(lib.ssm_decode_fused_workspace_bytes(ctypes.byref(d), rank))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    p = make_params(params)
+    st = lib.ssm_decode_fused(ctypes.byref(d), ctypes.byref(p), _ptr(w_x), _ptr(w_dt), rank, _ptr(x_t), _ptr(z_t),
+                              _ptr(y_t), _ptr(h), _ptr(conv), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), stream_handle(stream, dev))
+    if st != 0:
+        raise SsmError("ssm_decode_fused", st, lib.ssm_status_str(st).decode())
+    return y_t
 
 
 # ---- rate calibration (include/ssm_calib.h) ----

@@ -9,20 +9,12 @@
 // summed over the quad with two DPP adds.  Lane 0 of the quad writes y_t and the shifted
 // conv window.  Each quad owns its channel's cache entries, so the in-place update is
 // race-free.
+#include "ssm_decode_quad.h"
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
 namespace ssm {
 namespace {
-
-constexpr int QS = 4;  // states per lane
-
-__device__ __forceinline__ float quad_sum(float v) {
-  // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad ends with the quad's total.
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  return v;
-}
 
 constexpr int kDecodeBlock = 256;  // threads per workgroup (the launch below uses exactly this)
 
@@ -59,26 +51,10 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_quad(ScanArgs a) {
   // a select, so the step waits for one memory round trip, not a second one for z at the end.
   const float zt = to_f32(static_cast<const IO*>(a.z ? a.z : a.x)[row]);
 
-  const float v = cb + w.x * x0 + w.y * x1 + w.z * x2 + w.w * xt;
-  const float u = silu(v);
-  const float delta = softplus(dtr + dtb);
-  const float du = delta * u;
-  const float Aq[QS] = {A4.x, A4.y, A4.z, A4.w};
+  const float Bq[QS] = {to_f32(Bt[0]), to_f32(Bt[1]), to_f32(Bt[2]), to_f32(Bt[3])};
+  const float Cq[QS] = {to_f32(Ct[0]), to_f32(Ct[1]), to_f32(Ct[2]), to_f32(Ct[3])};
   float h[QS] = {h4.x, h4.y, h4.z, h4.w};
-  float r = 0.0f;
-#pragma unroll
-  for (int n = 0; n < QS; ++n) {
-    const float dA = hw_exp2(delta * (Aq[n] * kLog2e));
-    h[n] = fmaf(dA, h[n], du * to_f32(Bt[n]));
-    r = fmaf(to_f32(Ct[n]), h[n], r);
-  }
-  // Keep the D-skip and gate inputs out of the store branch below: the compiler would otherwise
-  // sink their loads into it, after the quad sum, and the step would wait for memory twice.
-  asm volatile("" ::"v"(dsk), "v"(zt));
-  r = quad_sum(r);
-  r = fmaf(dsk, u, r);
-  const float gz = silu(zt);
-  r *= a.z ? gz : 1.0f;
+  const float r = decode_quad_step(w, cb, dtb, dsk, A4, x0, x1, x2, xt, dtr, zt, a.z != nullptr, Bq, Cq, h);
   if (!live) return;
   *reinterpret_cast<float4*>(a.h_out + crow * 16 + q * QS) = make_float4(h[0], h[1], h[2], h[3]);
   if (q == 0) {

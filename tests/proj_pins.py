@@ -136,6 +136,35 @@ def check_conv_resume(P):
         assert np.array_equal(tail, full[:, :, L1:]), L1
 
 
+def _small_layer(seed):
+    """A small random layer (all sizes distinct): hidden [B, L1 + 1, d_model], weights, and
+    per-channel scan parameters, as plain arrays."""
+    g = _rng(seed)
+    Bs, L1, dm, d, r, n = 2, 9, 12, 8, 5, 4
+    w = {"in_x": g.standard_normal((d, dm)) / dm ** 0.5, "in_z": g.standard_normal((d, dm)) / dm ** 0.5,
+         "x_dt": g.standard_normal((r, d)) / d ** 0.5, "x_B": g.standard_normal((n, d)) / d ** 0.5,
+         "x_C": g.standard_normal((n, d)) / d ** 0.5, "dt": 0.5 * g.standard_normal((d, r)) / r ** 0.5,
+         "out": g.standard_normal((dm, d)) / d ** 0.5}
+    prm = {"A": -np.exp(g.uniform(-2, 2, (d, n))), "Dskip": g.uniform(0.25, 2.0, d),
+           "dt_bias": np.log(np.expm1(np.exp(g.uniform(np.log(1e-2), 0.0, d)))),
+           "conv_w": g.uniform(-0.5, 0.5, (d, 4)), "conv_b": g.uniform(-0.6, 0.6, d)}
+    return g.standard_normal((Bs, L1 + 1, dm)), w, prm, L1
+
+
+def check_layer_decode_is_next_token(P):
+    """The layer's caching invariant (page 1, Methodology item 3): decoding token L1 from the
+    cache a prefill of L1 tokens leaves gives what a prefill of L1 + 1 tokens gives at its last
+    token -- the out partial, and the final state and conv window -- bit for bit (every stage
+    computes each token's value by the same operations in both)."""
+    hidden, w, prm, L1 = _small_layer(10)
+    for io in ("f32", "bf16"):
+        out_full, h_full, c_full = P.layer_prefill(hidden, w, prm, io)
+        _, h1, c1 = P.layer_prefill(hidden[:, :L1], w, prm, io)
+        out_t, _, h2, c2 = P.layer_decode_step(hidden[:, L1], w, prm, h1, c1, io)
+        assert np.array_equal(out_t, out_full[:, L1]), (io, np.abs(out_t - out_full[:, L1]).max())
+        assert np.array_equal(h2, h_full) and np.array_equal(c2, c_full), io
+
+
 ALL_CHECKS = {
     "in_proj_brute": check_in_proj_brute,
     "x_proj_brute": check_x_proj_brute,
@@ -146,4 +175,5 @@ ALL_CHECKS = {
     "conv_silu_torch": check_conv_silu_torch,
     "conv_taps": check_conv_taps,
     "conv_resume": check_conv_resume,
+    "layer_decode_is_next_token": check_layer_decode_is_next_token,
 }

@@ -19,6 +19,13 @@ MUTANTS = {
     "conv0_ignored": ("hist = np.zeros((B, D, 3)) if conv0 is None else _f64(conv0)", "hist = np.zeros((B, D, 3))"),
     "silu_is_sigmoid": ("return v / (1.0 + np.exp(-v))", "return 1.0 / (1.0 + np.exp(-v))"),
     "history_reversed": ("xi = np.concatenate([hist, x], axis=2)", "xi = np.concatenate([hist[:, :, ::-1], x], axis=2)"),
+    "decode_conv_cache_ignored": ('u = to_io(conv_silu(x, params["conv_w"], params.get("conv_b"), _f64(conv)), io)',
+                                  'u = to_io(conv_silu(x, params["conv_w"], params.get("conv_b")), io)'),
+    "decode_gate_from_x": ('z = to_io(in_proj(hid, w["in_z"]), io)', 'z = to_io(in_proj(hid, w["in_x"]), io)'),
+    "decode_B_C_swapped": ('tok = {"x": x[..., 0], "dt": dt[..., 0], "z": z[..., 0], "Bm": Bm[:, 0], "Cm": Cm[:, 0]}',
+                           'tok = {"x": x[..., 0], "dt": dt[..., 0], "z": z[..., 0], "Bm": Cm[:, 0], "Cm": Bm[:, 0]}'),
+    "decode_dt_unrounded": ('dt = to_io(dt_proj(lowrank, w["dt"]), io)                          # [B, D, 1]',
+                            'dt = dt_proj(lowrank, w["dt"])                                     # [B, D, 1]'),
 }
 
 
@@ -34,7 +41,8 @@ def test_proj_pins_catch_mutant(name, source, tmp_path):
     assert source.count(old) >= 1, f"mutation site for {name} no longer in the projection oracle"
     path = tmp_path / "proj_mutant.py"
     path.write_text(source.replace(old, new, 1))
-    spec = importlib.util.spec_from_file_location("proj_mutant", str(path))
+    # named inside the oracle package, so that its layer compositions reach the scan oracle
+    spec = importlib.util.spec_from_file_location("oracle.proj_mutant", str(path))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     failed = []
