@@ -78,7 +78,9 @@ typedef enum {
   SSM_ERR_ALIGN = 4,     /* a tensor base pointer breaks the alignment rule below */
   SSM_ERR_ALIAS = 5,     /* an output overlaps an input or another output */
   SSM_ERR_WORKSPACE = 6, /* workspace NULL or smaller than ssm_prefill_workspace_bytes() */
-  SSM_ERR_LAUNCH = 7     /* a kernel launch failed (hipGetLastError) */
+  SSM_ERR_LAUNCH = 7,    /* a kernel launch failed (hipGetLastError) */
+  SSM_ERR_SCRATCH = 8    /* the call needs more scratch than a no-allocation entry point holds
+                            (ssm_decode_fused_noalloc: SSM_NOALLOC_SCRATCH_BYTES) */
 } ssm_status;
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;

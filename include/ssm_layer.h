@@ -58,6 +58,21 @@ ssm_status ssm_decode_fused(const ssm_dims* d, const ssm_params* p, const void* 
                             const void* x_t, const void* z_t, void* y_t, float* h, float* conv_state,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): ssm_decode_fused without a workspace argument.  Its
+ * scratch is a fixed array of SSM_NOALLOC_SCRATCH_BYTES in the library's device code, one per
+ * GPU, held until the process ends; its address is looked up on the first call on each device
+ * (with that device current) and kept.  The call allocates nothing.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must not be made; nothing in the array needs clearing (each call writes
+ * every byte it reads).  Sizes whose ssm_decode_fused_workspace_bytes() exceeds
+ * SSM_NOALLOC_SCRATCH_BYTES are rejected with SSM_ERR_SCRATCH before any HIP call.  Other
+ * arguments, errors and results as ssm_decode_fused (the same kernels). */
+#define SSM_NOALLOC_SCRATCH_BYTES (16u << 20)
+ssm_status ssm_decode_fused_noalloc(const ssm_dims* d, const ssm_params* p, const void* w_x, const void* w_dt,
+                                    int64_t rank, const void* x_t, const void* z_t, void* y_t, float* h,
+                                    float* conv_state, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ MAX_STATE = 16
 CONV_W = 4
 
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_DTYPE", 4: "SSM_ERR_ALIGN",
-          5: "SSM_ERR_ALIAS", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_LAUNCH"}
+          5: "SSM_ERR_ALIAS", 6: "SSM_ERR_WORKSPACE", 7: "SSM_ERR_LAUNCH", 8: "SSM_ERR_SCRATCH"}
 
 
 class SsmError(RuntimeError):
@@ -94,6 +94,9 @@ def load(path: str = LIB_PATH):
     lib.ssm_decode_fused.restype = ctypes.c_int
     lib.ssm_decode_fused.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params), vp, vp, i64] + [vp] * 5 + \
         [vp, sz, vp]
+    lib.ssm_decode_fused_noalloc.restype = ctypes.c_int
+    lib.ssm_decode_fused_noalloc.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Params), vp, vp, i64] + \
+        [vp] * 5 + [vp]
     lib.ssm_calib_issue.restype = ctypes.c_int
     lib.ssm_calib_issue.argtypes = [cint, i64, ctypes.c_int32, i64, vp, vp, vp]
     lib.ssm_calib_copy.restype = ctypes.c_int
@@ -481,6 +484,31 @@ def decode_fused(x_t, z_t, params: dict, w_x, w_dt, rank: int, h, conv, *, y_t=N
                               workspace.numel() * workspace.element_size(), stream_handle(stream, dev))
     if st != 0:
         raise SsmError("ssm_decode_fused", st, lib.ssm_status_str(st).decode())
+    return y_t
+
+
+def decode_fused_noalloc(x_t, z_t, params: dict, w_x, w_dt, rank: int, h, conv, *, y_t=None, stream=None):
+    """ssm_decode_fused_noalloc: as decode_fused, with the library's fixed per-GPU scratch instead
+    of a workspace (nothing is allocated; y_t must be given for no allocation at all)."""
+    lib = load()
+    Bsz, D = x_t.shape
+    N = params["A"].shape[1]
+    dev, io = x_t.device, x_t.dtype
+    _check(x_t, "x_t", (Bsz, D), io, dev)
+    _check(z_t, "z_t", (Bsz, D), io, dev, optional=True)
+    _check(w_x, "w_x", (rank + 2 * N, D), io, dev)
+    _check(w_dt, "w_dt", (D, rank), io, dev)
+    _check(h, "h", (Bsz, D, N), torch.float32, dev)
+    _check(conv, "conv", (Bsz, D, CONV_W - 1), torch.float32, dev)
+    _check_params(params, D, N, dev)
+    y_t = torch.empty_like(x_t) if y_t is None else y_t
+    _check(y_t, "y_t", (Bsz, D), io, dev)
+    d = Dims(Bsz, 1, D, N, CONV_W, _io_code(io), 0)
+    p = make_params(params)
+    st = lib.ssm_decode_fused_noalloc(ctypes.byref(d), ctypes.byref(p), _ptr(w_x), _ptr(w_dt), rank, _ptr(x_t),
+                                      _ptr(z_t), _ptr(y_t), _ptr(h), _ptr(conv), stream_handle(stream, dev))
+    if st != 0:
+        raise SsmError("ssm_decode_fused_noalloc", st, lib.ssm_status_str(st).decode())
     return y_t
 
 

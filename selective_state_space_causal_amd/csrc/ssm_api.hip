@@ -117,6 +117,7 @@ const char* ssm_status_str(int s) {
     case SSM_ERR_ALIAS: return "an output overlaps an input or another output";
     case SSM_ERR_WORKSPACE: return "workspace missing or smaller than ssm_prefill_workspace_bytes()";
     case SSM_ERR_LAUNCH: return "kernel launch failed";
+    case SSM_ERR_SCRATCH: return "the sizes need more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

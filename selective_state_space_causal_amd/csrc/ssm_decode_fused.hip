@@ -17,6 +17,8 @@
 // The step rewrites the conv cache that xproj_partial reads; the two launches are stream-ordered.
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ssm_layer.h"
 #include "ssm_decode_quad.h"
 #include "ssm_device.h"
@@ -251,45 +253,68 @@ bool fused_sizes(const ssm_dims* d, int64_t rank, int64_t* nblk, int64_t* ws_byt
   return true;
 }
 
-}  // namespace
-}  // namespace ssm
+// The no-allocation entry point's scratch: one array per GPU in this code object, loaded with
+// it and held until the process ends.  Host code never uses its name as an address (in host
+// code it is a stand-in for the device symbol): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept per device.
+constexpr size_t kScratchBytes = SSM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-extern "C" {
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipErrorUnknown;
+};
+ScratchSlot g_scratch[kMaxDevices];
 
-size_t ssm_decode_fused_workspace_bytes(const ssm_dims* d, int64_t rank) {
-  int64_t nblk, ws;
-  return ssm::fused_sizes(d, rank, &nblk, &ws) ? (size_t)ws : 0;
+// The current device's scratch address (looked up on its first use), or nullptr.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  return s.err == hipSuccess ? s.ptr : nullptr;
 }
 
-ssm_status ssm_decode_fused(const ssm_dims* d, const ssm_params* p, const void* w_x, const void* w_dt, int64_t rank,
-                            const void* x_t, const void* z_t, void* y_t, float* h, float* conv_state,
-                            void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace ssm;
+// Validation and launch shared by both entry points; ws == nullptr means the device scratch.
+ssm_status decode_fused(const ssm_dims* d, const ssm_params* p, const void* w_x, const void* w_dt, int64_t rank,
+                        const void* x_t, const void* z_t, void* y_t, float* h, float* conv_state, void* workspace,
+                        size_t workspace_bytes, bool use_scratch, void* stream) {
   if (!d) return SSM_ERR_NULL;
   int64_t nblk, ws_bytes;
   if (!fused_sizes(d, rank, &nblk, &ws_bytes)) return SSM_ERR_SHAPE;
   if (d->io_dtype != SSM_F32 && d->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (!p || !p->A || !p->Dskip || !p->dt_bias || !p->conv_w || !w_x || !w_dt || !x_t || !y_t || !h || !conv_state)
     return SSM_ERR_NULL;
-  if (!workspace || workspace_bytes < (size_t)ws_bytes) return SSM_ERR_WORKSPACE;
+  if (use_scratch) {
+    if ((size_t)ws_bytes > kScratchBytes) return SSM_ERR_SCRATCH;
+  } else if (!workspace || workspace_bytes < (size_t)ws_bytes) {
+    return SSM_ERR_WORKSPACE;
+  }
   const int64_t B = d->batch, D = d->d_inner, M = rank + 2 * kNS;
   const int64_t es = d->io_dtype == SSM_BF16 ? 2 : 4;
   const int64_t tok = B * D * es;
   const void* ins[9] = {x_t, z_t, w_x, w_dt, p->A, p->Dskip, p->dt_bias, p->conv_w, p->conv_b};
   const int64_t in_bytes[9] = {tok, tok, M * D * es, D * rank * es, D * kNS * 4, D * 4, D * 4, D * 16, D * 4};
   const uintptr_t in_align[9] = {(uintptr_t)es, (uintptr_t)es, (uintptr_t)es, (uintptr_t)es, 16, 4, 4, 16, 4};
+  const int nouts = use_scratch ? 3 : 4;
   void* outs[4] = {y_t, h, conv_state, workspace};
   const int64_t out_bytes[4] = {tok, B * D * kNS * 4, B * D * 3 * 4, ws_bytes};
   const uintptr_t out_align[4] = {(uintptr_t)es, 16, 4, 4};
   for (int i = 0; i < 9; ++i)
     if (ins[i] && !aligned(ins[i], in_align[i])) return SSM_ERR_ALIGN;
-  for (int o = 0; o < 4; ++o)
+  for (int o = 0; o < nouts; ++o)
     if (!aligned(outs[o], out_align[o])) return SSM_ERR_ALIGN;
-  for (int o = 0; o < 4; ++o) {
+  for (int o = 0; o < nouts; ++o) {
     for (int i = 0; i < 9; ++i)
       if (overlaps(span(outs[o], out_bytes[o]), span(ins[i], in_bytes[i]))) return SSM_ERR_ALIAS;
-    for (int q = o + 1; q < 4; ++q)
+    for (int q = o + 1; q < nouts; ++q)
       if (overlaps(span(outs[o], out_bytes[o]), span(outs[q], out_bytes[q]))) return SSM_ERR_ALIAS;
+  }
+  if (use_scratch) {
+    workspace = device_scratch();
+    if (!workspace) return SSM_ERR_LAUNCH;
   }
   FusedArgs a;
   memset(&a, 0, sizeof a);
@@ -317,6 +342,29 @@ ssm_status ssm_decode_fused(const ssm_dims* d, const ssm_params* p, const void* 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = d->io_dtype == SSM_BF16 ? launch<bf16_t>(a, vec_x, vec_dt, s) : launch<float>(a, vec_x, vec_dt, s);
   return e == hipSuccess ? SSM_OK : SSM_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" {
+
+size_t ssm_decode_fused_workspace_bytes(const ssm_dims* d, int64_t rank) {
+  int64_t nblk, ws;
+  return ssm::fused_sizes(d, rank, &nblk, &ws) ? (size_t)ws : 0;
+}
+
+ssm_status ssm_decode_fused(const ssm_dims* d, const ssm_params* p, const void* w_x, const void* w_dt, int64_t rank,
+                            const void* x_t, const void* z_t, void* y_t, float* h, float* conv_state,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return ssm::decode_fused(d, p, w_x, w_dt, rank, x_t, z_t, y_t, h, conv_state, workspace, workspace_bytes, false,
+                           stream);
+}
+
+ssm_status ssm_decode_fused_noalloc(const ssm_dims* d, const ssm_params* p, const void* w_x, const void* w_dt,
+                                    int64_t rank, const void* x_t, const void* z_t, void* y_t, float* h,
+                                    float* conv_state, void* stream) {
+  return ssm::decode_fused(d, p, w_x, w_dt, rank, x_t, z_t, y_t, h, conv_state, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

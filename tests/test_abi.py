@@ -39,8 +39,8 @@ def test_exports_every_declared_symbol():
 def test_version_and_status_strings():
     lib = L.load()
     assert lib.ssm_abi_version() == L.ABI_VERSION
-    for code in range(8):
-        assert lib.ssm_status_str(code)
+    for code in range(9):
+        assert lib.ssm_status_str(code) != b"unknown status", code
     assert lib.ssm_status_str(99) == b"unknown status"
 
 

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake-poin
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssm_layer.h")
 BASE, STEP = 0x7F0000000000, 1 << 32
-NULL, SHAPE, DTYPE, ALIGN, ALIAS, WS = 1, 2, 3, 4, 5, 6
+NULL, SHAPE, DTYPE, ALIGN, ALIAS, WS, SCRATCH = 1, 2, 3, 4, 5, 6, 8
 
 
 def fake(i, off=0):
@@ -47,7 +47,7 @@ def fused(d, p, rank=24, **over):
 def test_exports_every_declared_symbol():
     src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src)))
-    assert {"ssm_decode_fused", "ssm_decode_fused_workspace_bytes"} <= set(names)
+    assert {"ssm_decode_fused", "ssm_decode_fused_workspace_bytes", "ssm_decode_fused_noalloc"} <= set(names)
     lib = L.load()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ssm_layer.h but not exported"
@@ -88,3 +88,32 @@ def test_alignment_and_aliasing():
     assert fused(dims(), params(), y=fake(2)) == ALIAS               # y on x
     assert fused(dims(), params(), ws=fake(0)) == ALIAS              # workspace on the weights
     assert fused(dims(), params(), conv=fake(5, 1 << 12)) == ALIAS   # conv inside h
+
+
+def noalloc(d, p, rank=24, **over):
+    a = dict(wx=fake(0), wdt=fake(1), x=fake(2), z=fake(3), y=fake(4), h=fake(5), conv=fake(6))
+    a.update(over)
+    return L.load().ssm_decode_fused_noalloc(None if d is None else ctypes.byref(d),
+                                             None if p is None else ctypes.byref(p), a["wx"], a["wdt"], rank, a["x"],
+                                             a["z"], a["y"], a["h"], a["conv"], None)
+
+
+def test_noalloc_validation_and_scratch_limit():
+    """The no-allocation variant validates like ssm_decode_fused and refuses, before any HIP call,
+    sizes whose partial sums would not fit its fixed 16 MiB scratch."""
+    lib = L.load()
+    assert noalloc(None, params()) == NULL
+    assert noalloc(dims(), params(), y=None) == NULL
+    assert noalloc(dims(d_state=8), params()) == SHAPE
+    assert noalloc(dims(), params(), h=fake(5, 8)) == ALIGN
+    assert noalloc(dims(), params(), y=fake(2)) == ALIAS
+    limit = 16 << 20
+    # batch 1024 x 80 blocks of 64 channels x 288 outputs x 4 bytes = 94 MB: too much
+    big = dims(batch=1024, d_inner=5120)
+    assert lib.ssm_decode_fused_workspace_bytes(ctypes.byref(big), 256) > limit
+    assert noalloc(big, params(), rank=256) == SCRATCH
+    edge = dims(batch=183, d_inner=5120)   # 183 x 80 x 288 x 4 bytes > 16 MiB; 182 rows fit
+    assert lib.ssm_decode_fused_workspace_bytes(ctypes.byref(edge), 256) > limit
+    assert noalloc(edge, params(), rank=256) == SCRATCH
+    assert lib.ssm_decode_fused_workspace_bytes(ctypes.byref(dims(batch=182, d_inner=5120)), 256) <= limit
+    assert lib.ssm_status_str(SCRATCH) != b"unknown status"
