@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  It shares no code with
 the GPU library: the arithmetic lives in ``ssm_oracle.c`` (plain C, fp64,
-libm, one channel at a time, token after token), built here with gcc.
+libm, one channel at a time, token after token), built here with gcc (or, with
+SSM_SANITIZE=1, with clang under AddressSanitizer and UndefinedBehaviorSanitizer).
 
 What it follows: "Scaling State-Space Models on Multiple GPUs with Tensor
 Parallelism" (euno.news summary of arXiv 2602.21144), Methodology item 2
@@ -27,16 +28,25 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssm_oracle.c")
-_LIB = os.path.join(_HERE, "libssm_oracle.so")
+# SSM_SANITIZE=1: a clang build instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+# (the same sanitizer runtime as the library's sanitized build, which the process preloads).
+_SANITIZE = os.environ.get("SSM_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "libssm_oracle_san.so" if _SANITIZE else "libssm_oracle.so")
 _lib = None
 
 CONV_W = 4
 
 
 def build(verbose: bool = False) -> str:
-    """Compile ssm_oracle.c into oracle/libssm_oracle.so (no fast-math, no FMA contraction)."""
-    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
-           "-Wall", "-Wextra", "-o", _LIB, _SRC, "-lm", "-lpthread"]
+    """Compile ssm_oracle.c into oracle/libssm_oracle.so (no fast-math, no FMA contraction);
+    with SSM_SANITIZE=1, into oracle/libssm_oracle_san.so with clang and the sanitizers."""
+    if _SANITIZE:
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-fPIC", "-shared", "-std=c99", "-ffp-contract=off",
+               "-fno-fast-math", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-shared-libsan",
+               "-Wall", "-Wextra", "-o", _LIB, _SRC, "-lm", "-lpthread"]
+    else:
+        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+               "-Wall", "-Wextra", "-o", _LIB, _SRC, "-lm", "-lpthread"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

@@ -10,7 +10,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libssm.so")
+# SSM_SANITIZE=1 selects the host-sanitized build (build.py --sanitize; CPU test runs only).
+LIB_PATH = os.path.join(_HERE, "libssm_san.so" if os.environ.get("SSM_SANITIZE") == "1" else "libssm.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 ABI_VERSION = 2

@@ -34,13 +34,26 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# The sanitizer variant (libssm_san.so, loaded when SSM_SANITIZE=1): host code instrumented with
+# AddressSanitizer and UndefinedBehaviorSanitizer, device code unchanged; linked with clang++
+# against the shared clang sanitizer runtime, which the process preloads (the oracle's sanitizer
+# build uses the same runtime).  For CPU-only test runs of the host-side validation.
+SAN_LIB = os.path.join(PKG, "libssm_san.so")
+SAN_BUILD_DIR = os.path.join(ROOT, "_build", "san")
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+CLANGXX = "/opt/rocm/llvm/bin/clang++"
+
+
+def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
+    build_dir = SAN_BUILD_DIR if sanitize else BUILD_DIR
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
+    extra = SAN_HOST_FLAGS if sanitize else []
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [cc, *HIP_FLAGS, "-c", src, "-o", obj]
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        cmd = [cc, *HIP_FLAGS, *extra, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,14 +68,34 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(compile_one, sources()))
-    tmp = LIB + ".tmp"
-    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, *LINK_LIBS]
+    out = SAN_LIB if sanitize else LIB
+    tmp = out + ".tmp"
+    if sanitize:
+        san = "-fsanitize=address,undefined"
+        cmd = [CLANGXX, "-shared", "-fPIC", san, "-shared-libsan", "-o", tmp, *objs, "-L/opt/rocm/lib",
+               "-lamdhip64", *LINK_LIBS]
+    else:
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, *LINK_LIBS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime a sanitized test run preloads."""
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise FileNotFoundError("clang's libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm")
+    return found[-1]
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+
+    san = "--sanitize" in sys.argv
+    print(build(verbose=True, sanitize=san))
+    if san:
+        print(f"run the CPU tests with: SSM_SANITIZE=1 ASAN_OPTIONS=detect_leaks=0 LD_PRELOAD={sanitizer_runtime()} "
+              "python -m pytest tests -m 'not gpu'")
