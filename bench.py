@@ -127,7 +127,7 @@ def timed_steps(step, nevents, warmup, steps):
 # The sources each measured kernel is built from: a traffic record stays valid while these
 # files are unchanged (a change elsewhere in the library does not touch that kernel).
 KERNEL_SOURCES = {
-    "scan": ["ssm_windowed.hip", "ssm_decode.hip", "ssm_seq.hip", "ssm_device.h", "ssm_internal.h"],
+    "scan": ["ssm_windowed.hip", "ssm_decode.hip", "ssm_decode_quad.h", "ssm_seq.hip", "ssm_device.h", "ssm_internal.h"],
     "codec": ["ssm_codec.hip", "ssm_device.h"],
 }
 
