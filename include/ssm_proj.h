@@ -96,8 +96,10 @@ int ssm_conv_silu(const ssm_dims* dims, const ssm_params* params, const void* x,
  * row-major).  bf16 io only (SSM_ERR_DTYPE otherwise); the sums are fp32 (matrix cores) and
  * rounded to bf16 (nearest even) once.  Uses dims (batch, seqlen, d_inner, d_state, d_conv = 4,
  * io_dtype), params->conv_w / conv_b, conv0 as in ssm_conv_silu.
- * Sizes: d_inner and seqlen multiples of 8 (SSM_ERR_SHAPE otherwise), rank >= 1.
- * Alignment: x and w 16-byte, conv_w 16-byte, conv_b and conv0 4-byte, outputs 2-byte.
+ * Sizes: d_inner and seqlen multiples of 8, seqlen below 2^24, (rank + 2N) * d_inner * 2 bytes
+ * below 2 GiB, rank >= 1 (SSM_ERR_SHAPE otherwise).
+ * Alignment: x and w 16-byte, conv_w 16-byte, conv_b and conv0 4-byte, outputs 2-byte (outputs
+ * 16-byte aligned, with rank and N multiples of 8, are written in 16-byte pieces).
  * Outputs may not overlap the inputs or each other.
  * Passage: Methodology item 1 of the page cited above (the local mixing kernels and the
  * projection weights of one GPU's feature slice).

@@ -23,8 +23,17 @@
 //     channels 8 (l / 32) .. + 7 of both tiles; the padded row pitch (144 bytes) keeps them
 //     free of bank conflicts.  Rows past M are zero in the W tile, so the products are
 //     unconditional (a guard per block made each product wait for its operand read).
-// The next step's x, conv weights and W are loaded into registers while the current step
-// multiplies.  The sums are rounded to bf16 (nearest even) once, at the end.
+// The steps are software-pipelined so that the loads, the conv front and the products of
+// different steps overlap instead of running in turn:
+//   - x (with its conv weights) is loaded two steps ahead into one of two register sets, W one
+//     step ahead;
+//   - while a wave multiplies step s, it computes u of step s + 1 into the other u tile, a
+//     quarter after each of the four 16-channel slices of products (the matrix cores run a
+//     product while the vector units compute), then stores step s + 1's W into the other W
+//     tile; one barrier per step.
+// Loads are unconditional (indices clamped into the tensors, values past them replaced by
+// zero), so no lane branches around a load.  The sums are rounded to bf16 (nearest even) once,
+// at the end, staged through LDS and written as whole 16-byte pieces of the output rows.
 #include <string.h>
 
 #include "../../include/ssm_proj.h"
@@ -41,12 +50,15 @@ constexpr int MB = 10;                     // row blocks of 32 per workgroup (32
 constexpr int ROWS = MB * 32;
 constexpr int PITCH = KC + 8;              // bf16 per LDS row (144 bytes)
 constexpr int WCHUNKS = ROWS * KC / 8;     // 16-byte chunks of a W step tile
-constexpr int WPT = (WCHUNKS + THREADS - 1) / THREADS;
+constexpr int WPT = WCHUNKS / THREADS;     // chunks per thread
 constexpr int MB_PER_WAVE = MB / 2;        // row blocks per wave (two row-block sets)
+constexpr int OPITCH = ROWS + 8;           // bf16 per token row of the output staging tile
+static_assert(WCHUNKS % THREADS == 0, "W tile chunks must divide among the threads");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x3 __attribute__((ext_vector_type(3), aligned(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 struct XprojArgs {
@@ -65,7 +77,9 @@ struct XprojArgs {
 struct Tiles {
   uint16_t u[2][TT * PITCH];
   uint16_t w[2][ROWS * PITCH];
+  float c[2][5 * KC];  // conv weights of a step: [KC] float4 taps, then [KC] biases
 };
+static_assert(sizeof(uint16_t) * TT * OPITCH <= sizeof(Tiles), "output staging must fit in the tiles");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -73,95 +87,249 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 
 constexpr int CPT = KC / 32;  // channels per thread (c and c + 32)
 
-// One thread's share of a step's loads: 8 tokens (plus the 4 before) of channels c and c + 32
-// of x with their conv weights, and up to WPT 16-byte chunks of W.
-struct StepRegs {
+// One thread's x for one step: 8 tokens of channels c and c + 32 and the history before them:
+// the 6 raw inputs before the group (bf16 pairs, of which the last 3 are used) or, for a row's
+// first group, the 3 cached inputs (fp32).
+struct XRegs {
   u32x4 xv[CPT];
-  u32x2 xh[CPT];
-  float4 cw[CPT];
-  float cb[CPT];
-  u32x4 wv[WPT];
+  u32x3 xh[CPT];
 };
 
-__device__ __forceinline__ void load_step(const XprojArgs& a, int64_t b, int64_t t0, int64_t k0, int m0,
-                                          StepRegs& r) {
+// One thread's WPT 16-byte chunks of one step's W tile, and the conv taps and bias of one
+// channel of the step after it.
+struct WRegs {
+  u32x4 wv[WPT];
+  u32x4 cv;
+  uint32_t cb;
+};
+
+
+// Every thread issues the same loads in every step (no load sits under a branch), so that the
+// wait for a set loaded two steps ago leaves the later loads in flight.
+__device__ __forceinline__ void load_x(const XprojArgs& a, int64_t b, int64_t t0, int64_t k0, XRegs& r) {
   const int g = threadIdx.x >> 5;
+  const int64_t t = t0 + 8 * g;
+  // L and t are multiples of 8: a group of 8 tokens is wholly inside or past the row end, and
+  // the loads are naturally aligned.  Past the end the group reads the row's last 8 tokens.
+  const int64_t tl = t < a.L ? t : a.L - 8;
+  const bool head = t == 0 && a.conv0 != nullptr;  // history from the cache
+  // the step's block of channel rows through a buffer view (uniform base, 32-bit lane offsets;
+  // the offsets stay inside it, clamped as above)
+  const int rows = a.D - k0 < KC ? (int)(a.D - k0) : KC;
+  const auto rx = rsrc(static_cast<const char*>(a.x) + (b * a.D + k0) * a.L * 2, (int64_t)rows * a.L * 2);
 #pragma unroll
   for (int h = 0; h < CPT; ++h) {
     const int c = (threadIdx.x & 31) + 32 * h;
-    const int64_t ch = k0 + c;
-    r.xv[h] = u32x4{0u, 0u, 0u, 0u};
-    r.xh[h] = u32x2{0u, 0u};
-    r.cw[h] = float4{0.0f, 0.0f, 0.0f, 0.0f};
-    r.cb[h] = 0.0f;
-    if (ch < a.D) {
-      r.cw[h] = *reinterpret_cast<const float4*>(a.conv_w + ch * 4);
-      r.cb[h] = a.conv_b ? a.conv_b[ch] : 0.0f;
-      // L and t are multiples of 8: a group of 8 tokens is wholly inside or past the row end,
-      // and both loads are naturally aligned.
-      const uint16_t* xr = static_cast<const uint16_t*>(a.x) + (b * a.D + ch) * a.L;
-      const int64_t t = t0 + 8 * g;
-      if (t < a.L) r.xv[h] = *reinterpret_cast<const u32x4*>(xr + t);
-      if (t > 0 && t < a.L) r.xh[h] = *reinterpret_cast<const u32x2*>(xr + t - 4);
-    }
-  }
-  const auto rw = rsrc(a.w, (int64_t)a.M * a.D * 2);
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    const int ci = threadIdx.x + i * THREADS;  // chunk: row ci / (KC / 8), channels 8 (ci % (KC / 8)) ..
-    const int row = m0 + ci / (KC / 8), q = ci % (KC / 8);
-    r.wv[i] = u32x4{0u, 0u, 0u, 0u};
-    if (ci < WCHUNKS && row < a.M && k0 + 8 * q < a.D)
-      r.wv[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(((int64_t)row * a.D + k0 + 8 * q) * 2), 0, 0);
+    const int cc = c < rows ? c : rows - 1;
+    // raw values: channels past D give u = 0 in conv_piece, tokens past L only outputs that
+    // are not stored
+    r.xv[h] = __builtin_amdgcn_raw_buffer_load_b128(rx, (cc * (int)a.L + (int)tl) * 2, 0, 0);
+    // one load from one of two places (an address select, not a branch)
+    const uintptr_t px = reinterpret_cast<uintptr_t>(static_cast<const char*>(a.x) + (b * a.D + k0) * a.L * 2) +
+                         (uint32_t)((cc * (int)a.L + (tl >= 6 ? (int)tl - 6 : 0)) * 2);
+    const uintptr_t pc = reinterpret_cast<uintptr_t>(a.conv0) + (uint64_t)((b * a.D + k0 + cc) * 12);
+    r.xh[h] = *reinterpret_cast<const __attribute__((address_space(1))) u32x3*>(head ? pc : px);
   }
 }
 
-// u for this thread's 8 tokens of its two channels, bf16, into the transposed tile; W chunks
-// into the W tile.
-__device__ __forceinline__ void stage_step(const XprojArgs& a, int64_t b, int64_t t0, int64_t k0, const StepRegs& r,
-                                           uint16_t* ut, uint16_t* wt) {
-  const int g = threadIdx.x >> 5;
+// W chunks of step k0 (rows m0 ..), read from clamped places past M or D (store_w zeroes them).
+__device__ __forceinline__ void load_w(const XprojArgs& a, int64_t k0, int m0, WRegs& r) {
+  // 32-bit offsets: the caller keeps W below 2 GiB
+  const auto rw = rsrc(a.w, (int64_t)a.M * a.D * 2);
+  const int D = (int)a.D, k = (int)k0;
 #pragma unroll
-  for (int h = 0; h < CPT; ++h) {
-    const int c = (threadIdx.x & 31) + 32 * h;
-    const int64_t ch = k0 + c;
-    uint32_t o[4] = {0u, 0u, 0u, 0u};
-    if (ch < a.D) {
-      float xv[11];  // xv[0..2] = raw inputs t-3 .. t-1, xv[3 + j] = token t + j
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        xv[3 + 2 * k] = __uint_as_float(r.xv[h][k] << 16);
-        xv[4 + 2 * k] = __uint_as_float(r.xv[h][k] & 0xFFFF0000u);
-      }
-      const int64_t t = t0 + 8 * g;
-      if (t > 0) {
-        xv[0] = __uint_as_float(r.xh[h][0] & 0xFFFF0000u);
-        xv[1] = __uint_as_float(r.xh[h][1] << 16);
-        xv[2] = __uint_as_float(r.xh[h][1] & 0xFFFF0000u);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) xv[j] = a.conv0 ? a.conv0[(b * a.D + ch) * 3 + j] : 0.0f;
-      }
-      const float4 w4 = r.cw[h];
-      const float cb = r.cb[h];
-      float uv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = fmaf(w4.w, xv[3 + j], fmaf(w4.z, xv[2 + j], fmaf(w4.y, xv[1 + j], fmaf(w4.x, xv[j], cb))));
-        uv[j] = silu(v);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(o[k]) : "v"(uv[2 * k]), "v"(uv[2 * k + 1]));
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ut[(8 * g + j) * PITCH + c] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
+  for (int i = 0; i < WPT; ++i) {
+    const int ci = threadIdx.x + i * THREADS;  // chunk: row ci / (KC / 8), channels 8 (ci % (KC / 8)) ..
+    const int row = m0 + ci / (KC / 8);
+    const int kq = k + 8 * (ci % (KC / 8));
+    const int rr = row < a.M ? row : a.M - 1;
+    const int kk = kq < D ? kq : D - 8;
+    r.wv[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (rr * D + kk) * 2, 0, 0);
   }
+}
+
+// The conv weights of step kc: thread t reads channel kc + t % KC's taps (float4) and bias
+// (all threads the same loads; clamped past D, and without a bias the taps are read again).
+__device__ __forceinline__ void load_cw(const XprojArgs& a, int64_t kc, WRegs& r) {
+  const int last = (int)(a.D - 1 - kc);  // channels kc .. kc + last exist
+  const int i = threadIdx.x % KC;
+  const int ii = i <= last ? i : last;
+  const auto rw = rsrc(a.conv_w + kc * 4, (int64_t)(last + 1) * 16);
+  r.cv = __builtin_amdgcn_raw_buffer_load_b128(rw, ii * 16, 0, 0);
+  const auto rb = a.conv_b ? rsrc(a.conv_b + kc, (int64_t)(last + 1) * 4) : rw;
+  r.cb = __builtin_amdgcn_raw_buffer_load_b32(rb, ii * 4, 0, 0);
+}
+
+__device__ __forceinline__ void store_w(const XprojArgs& a, int64_t k0, int m0, const WRegs& r, uint16_t* wt) {
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
     const int ci = threadIdx.x + i * THREADS;
-    if (ci < WCHUNKS) *reinterpret_cast<u32x4*>(&wt[(ci / (KC / 8)) * PITCH + 8 * (ci % (KC / 8))]) = r.wv[i];
+    const bool ok = m0 + ci / (KC / 8) < a.M && k0 + 8 * (ci % (KC / 8)) < a.D;
+    *reinterpret_cast<u32x4*>(&wt[(ci / (KC / 8)) * PITCH + 8 * (ci % (KC / 8))]) = ok ? r.wv[i] : u32x4{0u, 0u, 0u, 0u};
   }
+}
+
+// Threads 0 .. KC - 1 store their channel's taps and bias ([KC] float4, then [KC] float).
+__device__ __forceinline__ void store_cw(const XprojArgs& a, int64_t kc, const WRegs& r, float* ct) {
+  const int t = threadIdx.x;
+  if (t < KC) {
+    const bool ok = t <= (int)(a.D - 1 - kc);
+    *reinterpret_cast<u32x4*>(&ct[4 * t]) = ok ? r.cv : u32x4{0u, 0u, 0u, 0u};
+    ct[4 * KC + t] = ok && a.conv_b ? __uint_as_float(r.cb) : 0.0f;
+  }
+}
+
+// u of tokens 4 HALF .. 4 HALF + 3 of this thread's channel H, bf16, into the transposed tile
+// (nch: channels of the step below D).
+template <int H, int HALF>
+__device__ __forceinline__ void conv_piece(const XRegs& r, bool head, bool cache, int nch, const float* ct,
+                                           uint16_t* ut) {
+  const int g = threadIdx.x >> 5;
+  const int c = (threadIdx.x & 31) + 32 * H;
+  float xv[7];  // raw inputs at window positions 4 HALF .. 4 HALF + 6 (positions 0..2 precede the group)
+  if (HALF == 0) {
+    if (head) {  // a row's first group: the cached inputs (zero without a cache)
+      xv[0] = cache ? __uint_as_float(r.xh[H][0]) : 0.0f;
+      xv[1] = cache ? __uint_as_float(r.xh[H][1]) : 0.0f;
+      xv[2] = cache ? __uint_as_float(r.xh[H][2]) : 0.0f;
+    } else {  // tokens t - 3 .. t - 1: the high half of the second pair and the third pair
+      xv[0] = __uint_as_float(r.xh[H][1] & 0xFFFF0000u);
+      xv[1] = __uint_as_float(r.xh[H][2] << 16);
+      xv[2] = __uint_as_float(r.xh[H][2] & 0xFFFF0000u);
+    }
+    xv[3] = __uint_as_float(r.xv[H][0] << 16);
+    xv[4] = __uint_as_float(r.xv[H][0] & 0xFFFF0000u);
+    xv[5] = __uint_as_float(r.xv[H][1] << 16);
+    xv[6] = __uint_as_float(r.xv[H][1] & 0xFFFF0000u);
+  } else {
+    xv[0] = __uint_as_float(r.xv[H][0] & 0xFFFF0000u);
+    xv[1] = __uint_as_float(r.xv[H][1] << 16);
+    xv[2] = __uint_as_float(r.xv[H][1] & 0xFFFF0000u);
+    xv[3] = __uint_as_float(r.xv[H][2] << 16);
+    xv[4] = __uint_as_float(r.xv[H][2] & 0xFFFF0000u);
+    xv[5] = __uint_as_float(r.xv[H][3] << 16);
+    xv[6] = __uint_as_float(r.xv[H][3] & 0xFFFF0000u);
+  }
+  const float4 w4 = *reinterpret_cast<const float4*>(&ct[4 * c]);
+  const float cb = ct[4 * KC + c];
+  float uv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float v = fmaf(w4.w, xv[3 + j], fmaf(w4.z, xv[2 + j], fmaf(w4.y, xv[1 + j], fmaf(w4.x, xv[j], cb))));
+    uv[j] = c < nch ? silu(v) : 0.0f;  // channels past D: exactly zero
+  }
+  uint32_t o[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(o[k]) : "v"(uv[2 * k]), "v"(uv[2 * k + 1]));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ut[(8 * g + 4 * HALF + j) * PITCH + c] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
+}
+
+// The products of one step on the tiles ut / wt, with u of the next step (nch channels below D)
+// computed into nu from X and the conv weights ct after each 16-channel slice.
+__device__ __forceinline__ void step_products(f32x16 (&acc)[MB_PER_WAVE], const uint16_t* ut, const uint16_t* wt,
+                                              int tb, int mset, const XRegs& X, bool head, bool cache, int nch,
+                                              const float* ct, uint16_t* nu) {
+  const int lane = threadIdx.x & 63;
+  const int frow = lane & 31, fk = 8 * (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < KC / 16; ++ks) {
+    const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&ut[(32 * tb + frow) * PITCH + 16 * ks + fk]);
+    bf16x8 aw[MB_PER_WAVE];  // rows past M are zero in the tile: their products are dropped at the end
+#pragma unroll
+    for (int i = 0; i < MB_PER_WAVE; ++i)
+      aw[i] = *reinterpret_cast<const bf16x8*>(&wt[(32 * (mset + 2 * i) + frow) * PITCH + 16 * ks + fk]);
+#pragma unroll
+    for (int i = 0; i < MB_PER_WAVE; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[i], bu, acc[i], 0, 0, 0);
+    if (ks == 0) conv_piece<0, 0>(X, head, cache, nch, ct, nu);
+    if (ks == 1) conv_piece<0, 1>(X, head, cache, nch, ct, nu);
+    if (ks == 2) conv_piece<1, 0>(X, head, cache, nch, ct, nu);
+    if (ks == 3) conv_piece<1, 1>(X, head, cache, nch, ct, nu);
+    __builtin_amdgcn_sched_barrier(0);  // keep each slice's operand reads with its products
+  }
+}
+
+// One step of the pipeline on tiles P: products of step s; u of step s + 1 from XN (loaded two
+// steps ago) with conv weights c[P ^ 1]; loads of W for step s + 1 (stored into w[P ^ 1] at the
+// end), the conv weights of step s + 2 (into c[P], free since u of step s was made) and x of
+// step s + 2 into XL.  All of it runs in every step, past the last step on repeated data into
+// tiles that are no longer read: no load or wait then depends on a branch.
+template <int P>
+__device__ __forceinline__ void pipe_step(const XprojArgs& a, Tiles& tl, f32x16 (&acc)[MB_PER_WAVE], int64_t b,
+                                          int64_t t0, int m0, int tb, int mset, bool head, int s, int nsteps,
+                                          WRegs& W, XRegs& XL, const XRegs& XN) {
+  const bool next = s + 1 < nsteps, after = s + 2 < nsteps;
+  const int64_t kn = (int64_t)(next ? s + 1 : s) * KC;
+  const int64_t ka = (int64_t)(after ? s + 2 : nsteps - 1) * KC;
+  // issue order: what this step stores at its end first, x last (its wait is two steps away)
+  load_w(a, kn, m0, W);
+  load_cw(a, ka, W);
+  load_x(a, b, t0, ka, XL);
+  const int nch = a.D - kn < KC ? (int)(a.D - kn) : KC;
+  step_products(acc, tl.u[P], tl.w[P], tb, mset, XN, head, a.conv0 != nullptr, nch, tl.c[P ^ 1], tl.u[P ^ 1]);
+  store_w(a, kn, m0, W, tl.w[P ^ 1]);
+  store_cw(a, ka, W, tl.c[P]);
+  __syncthreads();
+}
+
+__device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, f32x16 (&acc)[MB_PER_WAVE], int64_t b,
+                                          int64_t t0, int m0, int tb, int mset) {
+  const int nsteps = (int)((a.D + KC - 1) / KC);
+  const bool head = t0 == 0 && (threadIdx.x >> 5) == 0;  // this thread's group starts a row
+  const bool cache = a.conv0 != nullptr;
+  XRegs X0, X1;
+  WRegs W;
+  load_w(a, 0, m0, W);
+  load_cw(a, 0, W);
+  load_x(a, b, t0, 0, X0);
+  load_x(a, b, t0, nsteps > 1 ? KC : 0, X1);
+  store_w(a, 0, m0, W, tl.w[0]);
+  store_cw(a, 0, W, tl.c[0]);
+  if (nsteps > 1) {
+    load_cw(a, KC, W);
+    store_cw(a, KC, W, tl.c[1]);
+  }
+  __syncthreads();
+  const int nch0 = a.D < KC ? (int)a.D : KC;
+  conv_piece<0, 0>(X0, head, cache, nch0, tl.c[0], tl.u[0]);
+  conv_piece<0, 1>(X0, head, cache, nch0, tl.c[0], tl.u[0]);
+  conv_piece<1, 0>(X0, head, cache, nch0, tl.c[0], tl.u[0]);
+  conv_piece<1, 1>(X0, head, cache, nch0, tl.c[0], tl.u[0]);
+  __syncthreads();
+  // Two steps per trip, so that each register set and tile has a fixed role in each half.
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    pipe_step<0>(a, tl, acc, b, t0, m0, tb, mset, head, s, nsteps, W, X0, X1);
+    pipe_step<1>(a, tl, acc, b, t0, m0, tb, mset, head, s + 1, nsteps, W, X1, X0);
+  }
+  if (s < nsteps) pipe_step<0>(a, tl, acc, b, t0, m0, tb, mset, head, s, nsteps, W, X0, X1);
+}
+
+// Copy rows [lo, hi) of the stacked output (tensor `out`, width hi - lo) held in the staging
+// tile for this workgroup's ntok tokens: V = 8 moves whole 16-byte pieces (each token's run
+// starts 16-byte aligned and is a multiple of 8 long), V = 1 single elements.
+template <int V>
+__device__ __forceinline__ void copy_rows(const uint16_t* ot, uint16_t* out, int64_t tok0, int ntok, int m0, int lo,
+                                          int hi) {
+  const int a0 = lo > m0 ? lo : m0, a1 = hi < m0 + ROWS ? hi : m0 + ROWS;
+  if (a0 >= a1) return;
+  const int width = hi - lo, run = (a1 - a0) / V;
+  const int total = ntok * run;
+  for (int e = threadIdx.x; e < total; e += THREADS) {
+    const int tok = e / run, col = V * (e - tok * run);
+    const uint16_t* src = &ot[tok * OPITCH + (a0 - m0) + col];
+    uint16_t* dst = out + (tok0 + tok) * width + (a0 - lo) + col;
+    if (V == 8)
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    else
+      *dst = *src;
+  }
+}
+
+__device__ __forceinline__ bool vec_ok(const void* out, int m0, int lo, int hi) {
+  const int a0 = lo > m0 ? lo : m0, a1 = hi < m0 + ROWS ? hi : m0 + ROWS;
+  return ((hi - lo) % 8 == 0) && ((a0 - lo) % 8 == 0) && ((a1 - a0) % 8 == 0) && ((a0 - m0) % 8 == 0) &&
+         (reinterpret_cast<uintptr_t>(out) & 15) == 0;
 }
 
 __global__ __launch_bounds__(THREADS) void conv_xproj_kernel(XprojArgs a) {
@@ -173,60 +341,40 @@ __global__ __launch_bounds__(THREADS) void conv_xproj_kernel(XprojArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tb = wave & 3, mset = wave >> 2;
-  const int nsteps = (int)((a.D + KC - 1) / KC);
 
   f32x16 acc[MB_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < MB_PER_WAVE; ++i) acc[i] = f32x16{};
+  main_loop(a, tl, acc, b, t0, m0, tb, mset);
 
-  StepRegs r;
-  load_step(a, b, t0, 0, m0, r);
-  stage_step(a, b, t0, 0, r, tl.u[0], tl.w[0]);
-  __syncthreads();
-  const int frow = lane & 31, fk = 8 * (lane >> 5);
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) load_step(a, b, t0, (int64_t)(s + 1) * KC, m0, r);
-#pragma unroll
-    for (int ks = 0; ks < KC / 16; ++ks) {
-      const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&tl.u[cur][(32 * tb + frow) * PITCH + 16 * ks + fk]);
-      bf16x8 aw[MB_PER_WAVE];  // rows past M are zero in the tile: their products are dropped at the end
-#pragma unroll
-      for (int i = 0; i < MB_PER_WAVE; ++i)
-        aw[i] = *reinterpret_cast<const bf16x8*>(&tl.w[cur][(32 * (mset + 2 * i) + frow) * PITCH + 16 * ks + fk]);
-#pragma unroll
-      for (int i = 0; i < MB_PER_WAVE; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[i], bu, acc[i], 0, 0, 0);
-    }
-    if (more) stage_step(a, b, t0, (int64_t)(s + 1) * KC, r, tl.u[cur ^ 1], tl.w[cur ^ 1]);
-    __syncthreads();
-  }
-
-  // acc[i] register j: row 32 blk + 8 (j / 4) + 4 (lane / 32) + j % 4, token 32 tb + lane % 32.
-  const int64_t t = t0 + 32 * tb + (lane & 31);
-  if (t >= a.L) return;
-  const int64_t row_tok = b * a.L + t;  // one token row per lane: plain global stores
-  uint16_t* o0 = static_cast<uint16_t*>(a.out0) + row_tok * a.R;
-  uint16_t* o1 = static_cast<uint16_t*>(a.out1) + row_tok * a.N;
-  uint16_t* o2 = static_cast<uint16_t*>(a.out2) + row_tok * a.N;
+  // Stage the sums, rounded to bf16, as [token][row] (the last barrier of the loop has freed
+  // the tiles): acc[i] register j is row 32 blk + 8 (j / 4) + 4 (lane / 32) + j % 4 of token
+  // 32 tb + lane % 32, and registers j, j + 1 are adjacent rows.
+  uint16_t* ot = reinterpret_cast<uint16_t*>(&tl);
+  const int tok = 32 * tb + (lane & 31);
 #pragma unroll
   for (int i = 0; i < MB_PER_WAVE; ++i) {
     const int blk = mset + 2 * i;
-    if (m0 + 32 * blk >= a.M) continue;
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
-      const int m = m0 + 32 * blk + 8 * (j / 4) + 4 * (lane >> 5) + j % 4;  // m and m + 1
+      const int m = 32 * blk + 8 * (j / 4) + 4 * (lane >> 5) + j % 4;
       uint32_t pk;
       asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(pk) : "v"(acc[i][j]), "v"(acc[i][j + 1]));
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int mm = m + h;
-        const unsigned short v = (unsigned short)(pk >> (16 * h));
-        if (mm < a.R) o0[mm] = v;
-        else if (mm < a.R + a.N) o1[mm - a.R] = v;
-        else if (mm < a.M) o2[mm - a.R - a.N] = v;
-      }
+      *reinterpret_cast<uint32_t*>(&ot[tok * OPITCH + m]) = pk;
     }
+  }
+  __syncthreads();
+  const int ntok = (int)((a.L - t0) < TT ? (a.L - t0) : TT);
+  const int64_t tok0 = b * a.L + t0;
+  uint16_t* outs[3] = {static_cast<uint16_t*>(a.out0), static_cast<uint16_t*>(a.out1),
+                       static_cast<uint16_t*>(a.out2)};
+  const int lo[3] = {0, a.R, a.R + a.N}, hi[3] = {a.R, a.R + a.N, a.M};
+#pragma unroll
+  for (int o = 0; o < 3; ++o) {
+    if (vec_ok(outs[o], m0, lo[o], hi[o]))
+      copy_rows<8>(ot, outs[o], tok0, ntok, m0, lo[o], hi[o]);
+    else
+      copy_rows<1>(ot, outs[o], tok0, ntok, m0, lo[o], hi[o]);
   }
 }
 
@@ -249,13 +397,13 @@ extern "C" int ssm_conv_xproj(const ssm_dims* d, const ssm_params* p, const void
   if (d->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (rank > ((int64_t)1 << 20)) return SSM_ERR_SHAPE;
   const int64_t M = rank + 2 * d->d_state;
-  // Per-row buffer views are 32-bit: a channel row of x, the whole of W and one token's row of
-  // each output must stay below 2 GiB; the grid holds batch * ceil(L / 128) workgroups.
+  // Buffer views and lane offsets are 32-bit: 64 channel rows of x and the whole of W must stay
+  // below 2 GiB (seqlen below 2^24); the grid holds batch * ceil(L / 128) workgroups.
   int64_t rows, xbytes, tok, ob0, ob1;
   if (__builtin_mul_overflow(d->batch, d->d_inner, &rows) || __builtin_mul_overflow(rows, d->seqlen, &xbytes) ||
       __builtin_mul_overflow(xbytes, (int64_t)2, &xbytes) || __builtin_mul_overflow(d->batch, d->seqlen, &tok) ||
       __builtin_mul_overflow(tok, rank * 2, &ob0) || __builtin_mul_overflow(tok, d->d_state * 2, &ob1) ||
-      d->seqlen * 2 >= ((int64_t)1 << 31) - 2 * TT || M * d->d_inner * 2 >= ((int64_t)1 << 31) ||
+      d->seqlen * 2 * KC >= ((int64_t)1 << 31) || M * d->d_inner * 2 >= ((int64_t)1 << 31) ||
       d->batch > INT32_MAX / ((d->seqlen + TT - 1) / TT))
     return SSM_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(p->conv_w, 16) || (p->conv_b && !aligned(p->conv_b, 4)) ||

@@ -163,7 +163,8 @@ def conv_magnitude(x, conv_w, conv_b, conv0):
     hist = np.zeros((B, D, 3)) if conv0 is None else np.abs(conv0)
     xi = np.concatenate([hist, xa], axis=2)
     wa = np.abs(conv_w.double().numpy())
-    m = np.broadcast_to(np.abs(conv_b.double().numpy())[None, :, None], (B, D, Ls)).copy()
+    m = np.zeros((B, D, Ls)) if conv_b is None else \
+        np.broadcast_to(np.abs(conv_b.double().numpy())[None, :, None], (B, D, Ls)).copy()
     for k in range(4):
         m += wa[None, :, k, None] * xi[:, :, k:k + Ls]
     return m
@@ -215,6 +216,38 @@ def test_conv_xproj_matches_oracle(B, Ls, D, R, N, resume):
     assert np.all(err <= b), f"{i}: gpu {got[i]!r} ref {ref[i]!r} bound {b[i]:.3e}"
     note(f"conv_xproj: u elements with an open rounding: {int((bf16_flip_ulps(u64, scale) > 0).sum())} "
          f"of {u64.size}")
+
+
+def test_conv_xproj_no_bias_and_unaligned_outputs():
+    """Ragged channels and tokens (D 136 = 2 x 64 + 8, L 264 = 2 x 128 + 8), no conv bias, and
+    outputs that are views one element into larger buffers (2-byte aligned only, so written one
+    element at a time): equal bit for bit to the call with aligned outputs, which is held to the
+    oracle with the bound of test_conv_xproj_matches_oracle."""
+    B, Ls, D, R, N = 2, 264, 136, 24, 16
+    prm = I.make_params_distinct(D, N, seed=5)
+    prm["conv_b"] = None
+    g = torch.Generator().manual_seed(55)
+    x = torch.randn(B, D, Ls, generator=g).to(torch.bfloat16)
+    w = (torch.randn(R + 2 * N, D, generator=g) / D ** 0.5).to(torch.bfloat16)
+    pd = {k: v.to(DEV) for k, v in prm.items() if v is not None}
+    lr, Bm, Cm = L.conv_xproj(x.to(DEV), pd, w.to(DEV), R)
+    bufs = [torch.full((B * Ls * n + 1,), float("nan"), dtype=torch.bfloat16, device=DEV) for n in (R, N, N)]
+    views = [bf[1:].view(B, Ls, n) for bf, n in zip(bufs, (R, N, N))]
+    L.conv_xproj(x.to(DEV), pd, w.to(DEV), R, lowrank=views[0], Bm=views[1], Cm=views[2])
+    torch.cuda.synchronize()
+    for a, v, bf in zip((lr, Bm, Cm), views, bufs):
+        assert torch.equal(a.view(torch.int16), v.view(torch.int16))
+        assert torch.isnan(bf[0])                                   # nothing written before the view
+    u64 = P.conv_silu(x, prm["conv_w"], None, None)
+    scale = conv_magnitude(x, prm["conv_w"], None, None)
+    ub = P.to_io(u64, "bf16")
+    ref = P.x_proj(ub, w)
+    mag = P.x_proj(np.abs(ub), np.abs(w.double().numpy()))
+    flips = P.x_proj(bf16_flip_ulps(u64, scale), np.abs(w.double().numpy()))
+    b = D * U * mag + flips
+    b = b + 2.0 ** -8 * (np.abs(ref) + b)
+    got = torch.cat([lr, Bm, Cm], dim=2).double().cpu().numpy()
+    assert np.all(np.abs(got - ref) <= b)
 
 
 def test_conv_xproj_errors():
