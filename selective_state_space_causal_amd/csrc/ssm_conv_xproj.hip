@@ -56,6 +56,8 @@ constexpr int OPITCH = ROWS + 8;           // bf16 per token row of the output s
 static_assert(WCHUNKS % THREADS == 0, "W tile chunks must divide among the threads");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x3 __attribute__((ext_vector_type(3), aligned(4)));
@@ -179,24 +181,37 @@ __device__ __forceinline__ void store_cw(const XprojArgs& a, int64_t kc, const W
   }
 }
 
+// The conv taps and biases of this thread's two channels for one step.
+struct ConvW {
+  float4 w[CPT];
+  float b[CPT];
+};
+
+__device__ __forceinline__ ConvW read_convw(const float* ct) {
+  ConvW q;
+#pragma unroll
+  for (int h = 0; h < CPT; ++h) {
+    const int c = (threadIdx.x & 31) + 32 * h;
+    q.w[h] = *reinterpret_cast<const float4*>(&ct[4 * c]);
+    q.b[h] = ct[4 * KC + c];
+  }
+  return q;
+}
+
 // u of tokens 4 HALF .. 4 HALF + 3 of this thread's channel H, bf16, into the transposed tile
 // (nch: channels of the step below D).
 template <int H, int HALF>
-__device__ __forceinline__ void conv_piece(const XRegs& r, bool head, bool cache, int nch, const float* ct,
+__device__ __forceinline__ void conv_piece(const XRegs& r, const ConvW& q, bool head, bool cache, int nch,
                                            uint16_t* ut) {
   const int g = threadIdx.x >> 5;
   const int c = (threadIdx.x & 31) + 32 * H;
   float xv[7];  // raw inputs at window positions 4 HALF .. 4 HALF + 6 (positions 0..2 precede the group)
   if (HALF == 0) {
-    if (head) {  // a row's first group: the cached inputs (zero without a cache)
-      xv[0] = cache ? __uint_as_float(r.xh[H][0]) : 0.0f;
-      xv[1] = cache ? __uint_as_float(r.xh[H][1]) : 0.0f;
-      xv[2] = cache ? __uint_as_float(r.xh[H][2]) : 0.0f;
-    } else {  // tokens t - 3 .. t - 1: the high half of the second pair and the third pair
-      xv[0] = __uint_as_float(r.xh[H][1] & 0xFFFF0000u);
-      xv[1] = __uint_as_float(r.xh[H][2] << 16);
-      xv[2] = __uint_as_float(r.xh[H][2] & 0xFFFF0000u);
-    }
+    // a row's first group (head) takes the cached inputs (zero without a cache); the others
+    // tokens t - 3 .. t - 1: the high half of the second pair and the third pair
+    xv[0] = head ? (cache ? __uint_as_float(r.xh[H][0]) : 0.0f) : __uint_as_float(r.xh[H][1] & 0xFFFF0000u);
+    xv[1] = head ? (cache ? __uint_as_float(r.xh[H][1]) : 0.0f) : __uint_as_float(r.xh[H][2] << 16);
+    xv[2] = head ? (cache ? __uint_as_float(r.xh[H][2]) : 0.0f) : __uint_as_float(r.xh[H][2] & 0xFFFF0000u);
     xv[3] = __uint_as_float(r.xv[H][0] << 16);
     xv[4] = __uint_as_float(r.xv[H][0] & 0xFFFF0000u);
     xv[5] = __uint_as_float(r.xv[H][1] << 16);
@@ -210,42 +225,60 @@ __device__ __forceinline__ void conv_piece(const XRegs& r, bool head, bool cache
     xv[5] = __uint_as_float(r.xv[H][3] << 16);
     xv[6] = __uint_as_float(r.xv[H][3] & 0xFFFF0000u);
   }
-  const float4 w4 = *reinterpret_cast<const float4*>(&ct[4 * c]);
-  const float cb = ct[4 * KC + c];
-  float uv[4];
+  const float4 w4 = q.w[H];
+  const float cb = q.b[H];
+  f32x2 uv[2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float v = fmaf(w4.w, xv[3 + j], fmaf(w4.z, xv[2 + j], fmaf(w4.y, xv[1 + j], fmaf(w4.x, xv[j], cb))));
-    uv[j] = c < nch ? silu(v) : 0.0f;  // channels past D: exactly zero
+    uv[j >> 1][j & 1] = c < nch ? silu(v) : 0.0f;  // channels past D: exactly zero
   }
-  uint32_t o[2];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(o[k]) : "v"(uv[2 * k]), "v"(uv[2 * k + 1]));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ut[(8 * g + 4 * HALF + j) * PITCH + c] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
+  for (int k = 0; k < 2; ++k) {  // round to bf16, nearest even (v_cvt_pk_bf16_f32)
+    const uint32_t o = __builtin_bit_cast(uint32_t, __builtin_convertvector(uv[k], bf16x2));
+    ut[(8 * g + 4 * HALF + 2 * k) * PITCH + c] = (uint16_t)o;
+    ut[(8 * g + 4 * HALF + 2 * k + 1) * PITCH + c] = (uint16_t)(o >> 16);
+  }
 }
 
 // The products of one step on the tiles ut / wt, with u of the next step (nch channels below D)
-// computed into nu from X and the conv weights ct after each 16-channel slice.
+// computed into nu from X and the conv weights ct.  Per 16-channel slice: the operand fragments
+// of the next slice are read first, then the slice's five products are issued one at a time with
+// a quarter of the conv front's arithmetic between them (the matrix cores run a product while
+// the vector units compute), then that quarter's u is written.
 __device__ __forceinline__ void step_products(f32x16 (&acc)[MB_PER_WAVE], const uint16_t* ut, const uint16_t* wt,
                                               int tb, int mset, const XRegs& X, bool head, bool cache, int nch,
                                               const float* ct, uint16_t* nu) {
   const int lane = threadIdx.x & 63;
   const int frow = lane & 31, fk = 8 * (lane >> 5);
-#pragma unroll
-  for (int ks = 0; ks < KC / 16; ++ks) {
-    const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&ut[(32 * tb + frow) * PITCH + 16 * ks + fk]);
-    bf16x8 aw[MB_PER_WAVE];  // rows past M are zero in the tile: their products are dropped at the end
+  bf16x8 bu[2], aw[2][MB_PER_WAVE];  // rows past M are zero in the tile: their products are dropped
+  auto frags = [&](int ks, int f) {
+    bu[f] = *reinterpret_cast<const bf16x8*>(&ut[(32 * tb + frow) * PITCH + 16 * ks + fk]);
 #pragma unroll
     for (int i = 0; i < MB_PER_WAVE; ++i)
-      aw[i] = *reinterpret_cast<const bf16x8*>(&wt[(32 * (mset + 2 * i) + frow) * PITCH + 16 * ks + fk]);
+      aw[f][i] = *reinterpret_cast<const bf16x8*>(&wt[(32 * (mset + 2 * i) + frow) * PITCH + 16 * ks + fk]);
+  };
+  const ConvW q = read_convw(ct);
+  frags(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < MB_PER_WAVE; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[i], bu, acc[i], 0, 0, 0);
-    if (ks == 0) conv_piece<0, 0>(X, head, cache, nch, ct, nu);
-    if (ks == 1) conv_piece<0, 1>(X, head, cache, nch, ct, nu);
-    if (ks == 2) conv_piece<1, 0>(X, head, cache, nch, ct, nu);
-    if (ks == 3) conv_piece<1, 1>(X, head, cache, nch, ct, nu);
-    __builtin_amdgcn_sched_barrier(0);  // keep each slice's operand reads with its products
+  for (int ks = 0; ks < KC / 16; ++ks) {
+    const int f = ks & 1;
+    if (ks + 1 < KC / 16) frags(ks + 1, f ^ 1);
+#pragma unroll
+    for (int i = 0; i < MB_PER_WAVE; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[f][i], bu[f], acc[i], 0, 0, 0);
+    if (ks == 0) conv_piece<0, 0>(X, q, head, cache, nch, nu);
+    if (ks == 1) conv_piece<0, 1>(X, q, head, cache, nch, nu);
+    if (ks == 2) conv_piece<1, 0>(X, q, head, cache, nch, nu);
+    if (ks == 3) conv_piece<1, 1>(X, q, head, cache, nch, nu);
+    // order within the slice: next fragments, then product / arithmetic / product ...
+    if (ks + 1 < KC / 16) __builtin_amdgcn_sched_group_barrier(0x100, MB_PER_WAVE + 1, 0);
+#pragma unroll
+    for (int i = 0; i < MB_PER_WAVE; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -291,10 +324,11 @@ __device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, f32x16 
   }
   __syncthreads();
   const int nch0 = a.D < KC ? (int)a.D : KC;
-  conv_piece<0, 0>(X0, head, cache, nch0, tl.c[0], tl.u[0]);
-  conv_piece<0, 1>(X0, head, cache, nch0, tl.c[0], tl.u[0]);
-  conv_piece<1, 0>(X0, head, cache, nch0, tl.c[0], tl.u[0]);
-  conv_piece<1, 1>(X0, head, cache, nch0, tl.c[0], tl.u[0]);
+  const ConvW q0 = read_convw(tl.c[0]);
+  conv_piece<0, 0>(X0, q0, head, cache, nch0, tl.u[0]);
+  conv_piece<0, 1>(X0, q0, head, cache, nch0, tl.u[0]);
+  conv_piece<1, 0>(X0, q0, head, cache, nch0, tl.u[0]);
+  conv_piece<1, 1>(X0, q0, head, cache, nch0, tl.u[0]);
   __syncthreads();
   // Two steps per trip, so that each register set and tile has a fixed role in each half.
   int s = 0;
@@ -358,9 +392,8 @@ __global__ __launch_bounds__(THREADS) void conv_xproj_kernel(XprojArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
       const int m = 32 * blk + 8 * (j / 4) + 4 * (lane >> 5) + j % 4;
-      uint32_t pk;
-      asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(pk) : "v"(acc[i][j]), "v"(acc[i][j + 1]));
-      *reinterpret_cast<uint32_t*>(&ot[tok * OPITCH + m]) = pk;
+      const f32x2 pr = {acc[i][j], acc[i][j + 1]};
+      *reinterpret_cast<uint32_t*>(&ot[tok * OPITCH + m]) = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
     }
   }
   __syncthreads();
