@@ -28,6 +28,10 @@
  * (B = batch, L = seqlen, K = in_features, M = out_features; every tensor row-major and
  * contiguous.)  in_proj is called once for x (W = the x rows) and once for z; x_proj once per
  * output group (low-rank step input, B, C) so that each lands in its own contiguous tensor.
+ * With one token per batch row (seqlen 1, a decode step), batch <= 16 and K a multiple of 8
+ * (bf16) or 4 (fp32), both layouts are out[b, m] = sum_k W[m, k] in[b, k]: a matrix-vector
+ * product bound by reading W from HBM, which runs as a hand-written streaming kernel (fp32
+ * fused multiply-adds, W read once per 8 batch rows) instead of a GEMM.
  *
  * Conventions (as in ssm.h): device pointers owned by the caller; calls are stream-ordered
  * and asynchronous; arguments are validated on the host first, and an invalid call returns a

@@ -83,20 +83,19 @@ __global__ __launch_bounds__(kThreads) void xproj_partial(FusedArgs a) {
   const int64_t c0 = (int64_t)blk * kCB;
   const int ncb = (int)min((int64_t)kCB, a.D - c0);
   const bool full = VEC && ncb == kCB;
-  float wv[kRowsPerThread][kCB];  // this thread's rows' segments (full blocks only)
+  // This thread's rows' segments (full blocks only) as raw 16-byte pieces, unpacked only where
+  // they are used (after the barrier), so that their loads stay in flight with the conv front's.
+  constexpr int kPer = 16 / (int)sizeof(IO);
+  constexpr int kPieces = kCB / kPer;
+  u32x4 wraw[kRowsPerThread][kPieces];
   if (full) {
 #pragma unroll
     for (int k = 0; k < kRowsPerThread; ++k) {
       const int j = t + k * kThreads;
       if (j < a.M) {
-        const IO* wr = static_cast<const IO*>(a.wx) + (int64_t)j * a.D + c0;
+        const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const IO*>(a.wx) + (int64_t)j * a.D + c0);
 #pragma unroll
-        for (int i = 0; i < kCB; i += 8) {
-          float v8[8];
-          load8<IO>(wr + i, v8);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) wv[k][i + e] = v8[e];
-        }
+        for (int i = 0; i < kPieces; ++i) wraw[k][i] = wp[i];
       }
     }
   }
@@ -122,7 +121,21 @@ __global__ __launch_bounds__(kThreads) void xproj_partial(FusedArgs a) {
     float acc = 0.0f;
     if (full) {
 #pragma unroll
-      for (int i = 0; i < kCB; ++i) acc = fmaf(wv[k][i], us[i], acc);
+      for (int i = 0; i < kPieces; ++i) {
+        float v[kPer];
+        if constexpr (sizeof(IO) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(wraw[k][i][e] << 16);
+            v[2 * e + 1] = __uint_as_float(wraw[k][i][e] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(wraw[k][i][e]);
+        }
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) acc = fmaf(v[e], us[kPer * i + e], acc);
+      }
     } else {
       const IO* wr = static_cast<const IO*>(a.wx) + (int64_t)j * a.D + c0;
       for (int i = 0; i < ncb; ++i) acc = fmaf(to_f32(wr[i]), us[i], acc);
@@ -150,17 +163,16 @@ __global__ __launch_bounds__(kThreads) void dt_decode(FusedArgs a) {
   const int quarter = (a.R + 3) / 4;
   const int r0 = q * quarter, r1 = min(a.R, r0 + quarter);
   const IO* wr = static_cast<const IO*>(a.wdt) + c * a.R;
-  float wq[VEC ? kMaxQuarter : 1];
+  // The quarter row as raw 16-byte pieces, unpacked only where it is used (after the barrier),
+  // so that its loads stay in flight with the others below.
+  constexpr int kPer = 16 / (int)sizeof(IO);                 // weights per piece
+  constexpr int kPieces = (kMaxQuarter + kPer - 1) / kPer;
+  u32x4 wraw[VEC ? kPieces : 1];
   if (VEC) {
+    const u32x4* wp = reinterpret_cast<const u32x4*>(wr + r0);
 #pragma unroll
-    for (int i = 0; i < kMaxQuarter; i += 8) {
-      if (i < quarter) {
-        float v8[8];
-        load8<IO>(wr + r0 + i, v8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) wq[i + e] = v8[e];
-      }
-    }
+    for (int i = 0; i < kPieces; ++i)
+      if (i * kPer < quarter) wraw[i] = wp[i];
   }
   const int64_t row = b * a.D + c;
   const float4 w = *reinterpret_cast<const float4*>(a.conv_w + c * 4);
@@ -174,26 +186,53 @@ __global__ __launch_bounds__(kThreads) void dt_decode(FusedArgs a) {
   const float zt = to_f32(static_cast<const IO*>(a.z ? a.z : a.x)[row]);
 
   // This batch row's x_proj outputs: the blocks' partial sums in block order, rounded to io.
+  // A thread sums outputs t and t + kThreads (M <= 2 kThreads), both rows' partials loaded
+  // together, so the reads are one round trip per batch of partials (with clamped indices and
+  // the values past the end dropped, so that no load sits under a branch).
   const float* pb = a.part + b * a.nblk * a.M;
-  for (int j = t; j < a.M; j += kThreads) {
-    float s = 0.0f;
-    for (int k0 = 0; k0 < a.nblk; k0 += kPartBatch) {
-      float v[kPartBatch];
+  static_assert(kMaxRows <= 2 * kThreads, "two outputs per thread");
+  const int j0 = t, j1 = t + kThreads;
+  const int jc0 = j0 < a.M ? j0 : a.M - 1, jc1 = j1 < a.M ? j1 : a.M - 1;
+  float s0 = 0.0f, s1 = 0.0f;
+  for (int k0 = 0; k0 < a.nblk; k0 += kPartBatch) {
+    float v0[kPartBatch], v1[kPartBatch];
 #pragma unroll
-      for (int i = 0; i < kPartBatch; ++i) v[i] = k0 + i < a.nblk ? pb[(int64_t)(k0 + i) * a.M + j] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < kPartBatch; ++i) s += v[i];
+    for (int i = 0; i < kPartBatch; ++i) {
+      const int64_t k = k0 + i < a.nblk ? k0 + i : a.nblk - 1;
+      v0[i] = pb[k * a.M + jc0];
+      v1[i] = pb[k * a.M + jc1];
     }
-    rs[j] = to_f32(from_f32<IO>(s));
+#pragma unroll
+    for (int i = 0; i < kPartBatch; ++i) {  // blocks in order, as the unfused x_proj sums them
+      s0 += k0 + i < a.nblk ? v0[i] : 0.0f;
+      s1 += k0 + i < a.nblk ? v1[i] : 0.0f;
+    }
   }
+  if (j0 < a.M) rs[j0] = to_f32(from_f32<IO>(s0));
+  if (j1 < a.M) rs[j1] = to_f32(from_f32<IO>(s1));
   __syncthreads();
 
   // dt_proj of channel c: lane q sums its quarter of the row, the quad adds the quarters.
   float dtp = 0.0f;
   if (VEC) {
 #pragma unroll
-    for (int i = 0; i < kMaxQuarter; ++i)
-      if (i < quarter) dtp = fmaf(wq[i], rs[r0 + i], dtp);
+    for (int i = 0; i < kPieces; ++i) {
+      if (i * kPer < quarter) {
+        float v[kPer];
+        if constexpr (sizeof(IO) == 2) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(wraw[i][k] << 16);
+            v[2 * k + 1] = __uint_as_float(wraw[i][k] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = __uint_as_float(wraw[i][k]);
+        }
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) dtp = fmaf(v[e], rs[r0 + i * kPer + e], dtp);
+      }
+    }
   } else {
     for (int r = r0; r < r1; ++r) dtp = fmaf(to_f32(wr[r]), rs[r], dtp);
   }

@@ -1,6 +1,7 @@
 // ssm_proj.hip -- ssm_proj_* of include/ssm_proj.h: the channel-sliced projections around the
 // scan ("Scaling State-Space Models on Multiple GPUs with Tensor Parallelism", euno.news
-// summary of arXiv 2602.21144, Methodology items 1-2) as hipBLASLt GEMMs on the matrix cores.
+// summary of arXiv 2602.21144, Methodology items 1-2) as hipBLASLt GEMMs on the matrix cores,
+// except one-token calls (a decode step), which ssm_gemv.hip streams as matrix-vector products.
 //
 // hipBLASLt is column-major.  A row-major [R, C] matrix is a column-major [C, R] one, so:
 //   channel-major out (IN, DT): out_b[M, L] (row-major) is column-major [L, M] = in_b * W^T
@@ -18,6 +19,7 @@
 #include <vector>
 
 #include "../../include/ssm_proj.h"
+#include "ssm_gemv.h"
 
 namespace {
 
@@ -167,6 +169,12 @@ int ssm_proj(ssm_proj_ctx* ctx, int32_t kind, int64_t batch, int64_t seqlen, int
   if (!aligned16(in) || !aligned16(w) || !aligned16(out)) return SSM_ERR_ALIGN;
   if (overlaps(out, out_bytes, in, in_bytes) || overlaps(out, out_bytes, w, w_bytes)) return SSM_ERR_ALIAS;
   if (!workspace || workspace_bytes < kWorkspace) return SSM_ERR_WORKSPACE;
+  // One token per batch row (a decode step): a matrix-vector product, streamed by ssm_gemv.hip.
+  if (seqlen == 1 && ssm::gemv_fits(batch, in_features, out_features, io_dtype == SSM_BF16))
+    return ssm::gemv(io_dtype == SSM_BF16, out_dtype == SSM_BF16, batch, in_features, out_features, in, w, out,
+                     static_cast<hipStream_t>(stream))
+               ? SSM_OK
+               : SSM_ERR_LAUNCH;
   Plan* p = nullptr;
   if (!get_plan(ctx, kind, io_dtype, out_dtype, batch, seqlen, in_features, out_features, &p)) return SSM_ERR_LAUNCH;
   const float alpha = 1.0f, beta = 0.0f;

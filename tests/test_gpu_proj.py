@@ -44,7 +44,14 @@ def bound(kind, x, w, ref, out_bf16):
 
 @pytest.mark.parametrize("kind", [L.PROJ_IN, L.PROJ_X, L.PROJ_DT, L.PROJ_OUT])
 @pytest.mark.parametrize("io,od", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
-@pytest.mark.parametrize("B,Ls,K,M", [(2, 64, 32, 48), (1, 33, 17, 5), (3, 7, 3, 9), (2, 520, 96, 40)])
+@pytest.mark.parametrize("B,Ls,K,M", [(2, 64, 32, 48), (1, 33, 17, 5), (3, 7, 3, 9), (2, 520, 96, 40),
+                                      # one token per row: the streaming matrix-vector kernel (batch
+                                      # groups of 8, 4, 2, 1; ragged rows per wave and pieces per lane)
+                                      (1, 1, 4096, 64), (3, 1, 96, 40), (8, 1, 2048, 24), (11, 1, 64, 33),
+                                      (16, 1, 520, 17), (2, 1, 20, 7),
+                                      # ... and the GEMM when it does not apply (K not a whole
+                                      # number of 16-byte pieces, more than 16 rows)
+                                      (1, 1, 17, 5), (20, 1, 64, 16)])
 def test_projection_matches_oracle(pj, kind, io, od, B, Ls, K, M):
     note(f"proj {NAMES[kind]} io={io} out={od} B={B} L={Ls} K={K} M={M}")
     g = torch.Generator().manual_seed(B * 1000 + Ls * 10 + K + kind)
