@@ -37,43 +37,31 @@ struct ConvArgs {
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-template <typename IO>
-__device__ __forceinline__ float io_at(__amdgpu_buffer_rsrc_t r, int64_t i) {  // one element, 0 past the end
-  if constexpr (sizeof(IO) == 2)
-    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)(i * 2), 0, 0) << 16);
-  else
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)(i * 4), 0, 0));
-}
-
-// Lane g of the flattened (row, 8-token group) space.
+// Lane g of the flattened (row, 8-token group) space.  The lanes of a wave may belong to
+// different rows (rows shorter than 512 tokens), so every access is a plain global one with
+// its own 64-bit address (a buffer view per row would not be uniform over the wave).
 template <typename IO, bool ALIGNED>
 __device__ __forceinline__ void conv_lane(const ConvArgs& a, int64_t g) {
   const int64_t row = g / a.lanes_per_row;
   if (row >= a.rows) return;
   const int64_t t0 = (g - row * a.lanes_per_row) * EPL;
   const int64_t c = row % a.D;
-  const int64_t rb = a.L * (int64_t)sizeof(IO);
-  const auto rx = rsrc(static_cast<const IO*>(a.x) + row * a.L, rb);
-  const auto ru = rsrc(static_cast<IO*>(a.u) + row * a.L, rb);
+  const IO* xr = static_cast<const IO*>(a.x) + row * a.L;
 
   float xv[EPL + 3];  // xv[0..2] = raw inputs t0-3 .. t0-1, xv[3 + j] = token t0 + j
   if (t0 == 0) {
     for (int j = 0; j < 3; ++j) xv[j] = a.conv0 ? a.conv0[row * 3 + j] : 0.0f;
   }
-  if constexpr (ALIGNED) {
+  if constexpr (ALIGNED) {  // L is a multiple of the 16-byte piece: the lane's tokens are whole pieces
     if constexpr (sizeof(IO) == 2) {
-      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(t0 * 2), 0, 0);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(xr + t0);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         xv[3 + 2 * k] = __uint_as_float(w[k] << 16);
         xv[4 + 2 * k] = __uint_as_float(w[k] & 0xFFFF0000u);
       }
       if (t0 > 0) {  // tokens t0-4 .. t0-1 as one aligned 8-byte load; keep the last three
-        const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(rx, (int)((t0 - 4) * 2), 0, 0);
+        const u32x2 h = *reinterpret_cast<const u32x2*>(xr + t0 - 4);
         xv[0] = __uint_as_float(h[0] & 0xFFFF0000u);
         xv[1] = __uint_as_float(h[1] << 16);
         xv[2] = __uint_as_float(h[1] & 0xFFFF0000u);
@@ -81,23 +69,23 @@ __device__ __forceinline__ void conv_lane(const ConvArgs& a, int64_t g) {
     } else {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((t0 + 4 * hh) * 4), 0, 0);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(xr + t0 + 4 * hh);
 #pragma unroll
         for (int k = 0; k < 4; ++k) xv[3 + 4 * hh + k] = __uint_as_float(w[k]);
       }
       if (t0 > 0) {
-        const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((t0 - 4) * 4), 0, 0);
+        const u32x4 h = *reinterpret_cast<const u32x4*>(xr + t0 - 4);
         xv[0] = __uint_as_float(h[1]);
         xv[1] = __uint_as_float(h[2]);
         xv[2] = __uint_as_float(h[3]);
       }
     }
-  } else {
+  } else {  // element accesses; tokens past the row end read as zero
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) xv[3 + j] = io_at<IO>(rx, t0 + j);
+    for (int j = 0; j < EPL; ++j) xv[3 + j] = t0 + j < a.L ? to_f32(xr[t0 + j]) : 0.0f;
     if (t0 > 0) {
 #pragma unroll
-      for (int j = 0; j < 3; ++j) xv[j] = io_at<IO>(rx, t0 - 3 + j);
+      for (int j = 0; j < 3; ++j) xv[j] = to_f32(xr[t0 - 3 + j]);
     }
   }
 
@@ -111,32 +99,29 @@ __device__ __forceinline__ void conv_lane(const ConvArgs& a, int64_t g) {
   }
 
   const int nvalid = a.L - t0 < EPL ? (int)(a.L - t0) : EPL;
+  IO* ur = static_cast<IO*>(a.u) + row * a.L;
   if constexpr (sizeof(IO) == 2) {
     uint32_t o[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(o[k]) : "v"(uv[2 * k]), "v"(uv[2 * k + 1]));
     if (ALIGNED && nvalid == EPL) {
-      const u32x4 o4 = {o[0], o[1], o[2], o[3]};
-      __builtin_amdgcn_raw_buffer_store_b128(o4, ru, (int)(t0 * 2), 0, 0);
+      *reinterpret_cast<u32x4*>(ur + t0) = u32x4{o[0], o[1], o[2], o[3]};
     } else {
+      uint16_t* u16 = reinterpret_cast<uint16_t*>(ur);
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
-        if (j < nvalid)
-          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(o[j >> 1] >> (16 * (j & 1))), ru, (int)((t0 + j) * 2),
-                                                0, 0);
+        if (j < nvalid) u16[t0 + j] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
     }
   } else {
+    float* uf = reinterpret_cast<float*>(ur);
     if (ALIGNED && nvalid == EPL) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const u32x4 o4 = {__float_as_uint(uv[4 * hh]), __float_as_uint(uv[4 * hh + 1]), __float_as_uint(uv[4 * hh + 2]),
-                          __float_as_uint(uv[4 * hh + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(o4, ru, (int)((t0 + 4 * hh) * 4), 0, 0);
-      }
+      for (int hh = 0; hh < 2; ++hh)
+        *reinterpret_cast<float4*>(uf + t0 + 4 * hh) = make_float4(uv[4 * hh], uv[4 * hh + 1], uv[4 * hh + 2], uv[4 * hh + 3]);
     } else {
 #pragma unroll
       for (int j = 0; j < EPL; ++j)
-        if (j < nvalid) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(uv[j]), ru, (int)((t0 + j) * 4), 0, 0);
+        if (j < nvalid) uf[t0 + j] = uv[j];
     }
   }
 }
