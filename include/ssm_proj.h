@@ -33,8 +33,13 @@
  * product bound by reading W from HBM, which runs as a hand-written streaming kernel (fp32
  * fused multiply-adds, W read once per 8 batch rows) instead of a GEMM.
  *
+ * Algorithm choice: hipBLASLt's heuristic offers up to 8 algorithms per shape; for a shape of at
+ * least 1e10 flops the first ssm_proj call outside graph capture times each of them on the
+ * caller's buffers (two runs each, the host waiting on events) and the context keeps the fastest,
+ * so that call is slower and synchronous; later calls of the shape run the kept algorithm only.
+ *
  * Conventions (as in ssm.h): device pointers owned by the caller; calls are stream-ordered
- * and asynchronous; arguments are validated on the host first, and an invalid call returns a
+ * and asynchronous (but for the first call of a large shape, above); arguments are validated on the host first, and an invalid call returns a
  * non-zero ssm_status and enqueues nothing.  A projection context holds a hipBLASLt handle,
  * created for the device current at ssm_proj_create and valid only on it, and a cache of the
  * algorithm chosen per shape: create one per host thread (a context is not safe for

@@ -11,7 +11,8 @@
 //     where W is column-major [K, M] (op T) and in_b row-major [K, L] is column-major [L, K]
 //     (op T): m = M, n = L, k = K, lda = K, ldb = L, ldd = M.
 // The batch is a strided batch (the weight's batch stride is 0).  Algorithms are chosen once
-// per shape by hipBLASLt's heuristic and cached in the context.
+// per shape and cached in the context: hipBLASLt's heuristic offers up to 8, and for a shape of
+// at least 1e10 flops the first call times them and keeps the fastest.
 #include <hipblaslt/hipblaslt.h>
 #include <string.h>
 
@@ -25,12 +26,18 @@ namespace {
 
 constexpr size_t kWorkspace = size_t(64) << 20;  // device scratch a projection may use
 
+constexpr int kCandidates = 8;           // heuristic candidates timed on a large shape's first call
+constexpr double kTuneFlops = 1e10;      // shapes with fewer flops keep the heuristic's first choice
+
 struct Plan {
   int32_t kind, io, out;
   int64_t B, L, K, M;
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t a = nullptr, b = nullptr, d = nullptr;
   hipblasLtMatmulAlgo_t algo;
+  hipblasLtMatmulAlgo_t cand[kCandidates];
+  int ncand = 0;
+  bool tuned = false;
 };
 
 bool channel_major_out(int32_t kind) { return kind == SSM_PROJ_IN || kind == SSM_PROJ_DT; }
@@ -103,20 +110,56 @@ bool get_plan(ssm_proj_ctx* ctx, int32_t kind, int32_t io, int32_t out, int64_t 
   ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
        hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws, sizeof ws) ==
            HIPBLAS_STATUS_SUCCESS;
-  hipblasLtMatmulHeuristicResult_t heur[1];
+  hipblasLtMatmulHeuristicResult_t heur[kCandidates];
   int found = 0;
-  ok = ok && hipblasLtMatmulAlgoGetHeuristic(ctx->handle, p.desc, p.a, p.b, p.d, p.d, pref, 1, heur, &found) ==
-                 HIPBLAS_STATUS_SUCCESS &&
-       found > 0 && heur[0].workspaceSize <= kWorkspace;
+  ok = ok && hipblasLtMatmulAlgoGetHeuristic(ctx->handle, p.desc, p.a, p.b, p.d, p.d, pref, kCandidates, heur,
+                                             &found) == HIPBLAS_STATUS_SUCCESS;
   if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (!ok) {
+  for (int i = 0; ok && i < found; ++i)
+    if (heur[i].state == HIPBLAS_STATUS_SUCCESS && heur[i].workspaceSize <= kWorkspace) p.cand[p.ncand++] = heur[i].algo;
+  if (!ok || p.ncand == 0) {
     destroy_plan(p);
     return false;
   }
-  p.algo = heur[0].algo;
+  p.algo = p.cand[0];
+  p.tuned = p.ncand == 1 || 2.0 * (double)B * (double)L * (double)K * (double)M < kTuneFlops;
   ctx->plans.push_back(p);
   *result = &ctx->plans.back();
   return true;
+}
+
+// The first call of a large shape: time each heuristic candidate on the caller's own buffers
+// (one untimed run, then two between events on the stream; the host waits) and keep the fastest.
+// Skipped while the stream is being captured into a graph (the plan stays untuned until a call
+// outside capture); a candidate that fails to run is passed over.
+template <typename Run>
+void tune(Plan* p, hipStream_t s, Run run) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    p->tuned = true;
+    return;
+  }
+  float best = -1.0f;
+  int pick = 0;
+  for (int i = 0; i < p->ncand; ++i) {
+    if (run(&p->cand[i]) != HIPBLAS_STATUS_SUCCESS) continue;
+    float ms = 0.0f;
+    if (hipEventRecord(e0, s) != hipSuccess || run(&p->cand[i]) != HIPBLAS_STATUS_SUCCESS ||
+        run(&p->cand[i]) != HIPBLAS_STATUS_SUCCESS || hipEventRecord(e1, s) != hipSuccess ||
+        hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+      continue;
+    if (best < 0.0f || ms < best) {
+      best = ms;
+      pick = i;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  p->algo = p->cand[pick];
+  p->tuned = true;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -181,9 +224,13 @@ int ssm_proj(ssm_proj_ctx* ctx, int32_t kind, int64_t batch, int64_t seqlen, int
   const bool cm = channel_major_out(kind);
   const void* A = cm ? in : w;
   const void* Bop = cm ? w : in;
-  const hipblasStatus_t st = hipblasLtMatmul(ctx->handle, p->desc, &alpha, A, p->a, Bop, p->b, &beta, out, p->d, out,
-                                             p->d, &p->algo, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
-  return st == HIPBLAS_STATUS_SUCCESS ? SSM_OK : SSM_ERR_LAUNCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto run = [&](const hipblasLtMatmulAlgo_t* algo) {
+    return hipblasLtMatmul(ctx->handle, p->desc, &alpha, A, p->a, Bop, p->b, &beta, out, p->d, out, p->d, algo,
+                           workspace, workspace_bytes, s);
+  };
+  if (!p->tuned) tune(p, s, run);
+  return run(&p->algo) == HIPBLAS_STATUS_SUCCESS ? SSM_OK : SSM_ERR_LAUNCH;
 }
 
 }  // extern "C"
