@@ -21,8 +21,8 @@
 //     32 rows on the matrix cores: v_mfma_f32_32x32x16_bf16, fp32 accumulation, four per row
 //     block per step.  Operand fragments are 16-byte LDS reads: lane l takes row l % 32 and
 //     channels 8 (l / 32) .. + 7 of both tiles; the padded row pitch (144 bytes) keeps them
-//     free of bank conflicts.  Rows past M are zero in the W tile, so the products are
-//     unconditional (a guard per block made each product wait for its operand read).
+//     free of bank conflicts.  The products are unconditional (a guard per block made each product
+//     wait for its operand read): rows past M feed only outputs that are not stored.
 // The steps are software-pipelined so that the loads, the conv front and the products of
 // different steps overlap instead of running in turn:
 //   - x (with its conv weights) is loaded two steps ahead into one of two register sets, W one
@@ -31,8 +31,8 @@
 //     quarter after each of the four 16-channel slices of products (the matrix cores run a
 //     product while the vector units compute), then stores step s + 1's W into the other W
 //     tile; one barrier per step.
-// Loads are unconditional (indices clamped into the tensors, values past them replaced by
-// zero), so no lane branches around a load.  The sums are rounded to bf16 (nearest even) once,
+// Loads are unconditional (indices clamped into the tensors; u past D and W past D are zeroed
+// where they are consumed or stored), so no lane branches around a load.  The sums are rounded to bf16 (nearest even) once,
 // at the end, staged through LDS and written as whole 16-byte pieces of the output rows.
 #include <string.h>
 
@@ -134,7 +134,7 @@ __device__ __forceinline__ void load_x(const XprojArgs& a, int64_t b, int64_t t0
   }
 }
 
-// W chunks of step k0 (rows m0 ..), read from clamped places past M or D (store_w zeroes them).
+// W chunks of step k0 (rows m0 ..), read from clamped places past M or D (see store_w).
 __device__ __forceinline__ void load_w(const XprojArgs& a, int64_t k0, int m0, WRegs& r) {
   // 32-bit offsets: the caller keeps W below 2 GiB
   const auto rw = rsrc(a.w, (int64_t)a.M * a.D * 2);
@@ -162,12 +162,19 @@ __device__ __forceinline__ void load_cw(const XprojArgs& a, int64_t kc, WRegs& r
   r.cb = __builtin_amdgcn_raw_buffer_load_b32(rb, ii * 4, 0, 0);
 }
 
-__device__ __forceinline__ void store_w(const XprojArgs& a, int64_t k0, int m0, const WRegs& r, uint16_t* wt) {
+// Rows past M hold copies of row M - 1 (clamped reads): they feed only output rows past M, which
+// are never stored.  Channels past D are zeroed (the step that reaches past D only; a uniform
+// branch), so that they add nothing to the rows that are stored.
+__device__ __forceinline__ void store_w(const XprojArgs& a, int64_t k0, const WRegs& r, uint16_t* wt) {
+  const bool full = k0 + KC <= a.D;
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
     const int ci = threadIdx.x + i * THREADS;
-    const bool ok = m0 + ci / (KC / 8) < a.M && k0 + 8 * (ci % (KC / 8)) < a.D;
-    *reinterpret_cast<u32x4*>(&wt[(ci / (KC / 8)) * PITCH + 8 * (ci % (KC / 8))]) = ok ? r.wv[i] : u32x4{0u, 0u, 0u, 0u};
+    u32x4* dst = reinterpret_cast<u32x4*>(&wt[(ci / (KC / 8)) * PITCH + 8 * (ci % (KC / 8))]);
+    if (full)
+      *dst = r.wv[i];
+    else
+      *dst = k0 + 8 * (ci % (KC / 8)) < a.D ? r.wv[i] : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -251,7 +258,7 @@ __device__ __forceinline__ void step_products(f32x16 (&acc)[MB_PER_WAVE], const 
                                               const float* ct, uint16_t* nu) {
   const int lane = threadIdx.x & 63;
   const int frow = lane & 31, fk = 8 * (lane >> 5);
-  bf16x8 bu[2], aw[2][MB_PER_WAVE];  // rows past M are zero in the tile: their products are dropped
+  bf16x8 bu[2], aw[2][MB_PER_WAVE];  // rows past M feed only outputs that are dropped
   auto frags = [&](int ks, int f) {
     bu[f] = *reinterpret_cast<const bf16x8*>(&ut[(32 * tb + frow) * PITCH + 16 * ks + fk]);
 #pragma unroll
@@ -300,7 +307,7 @@ __device__ __forceinline__ void pipe_step(const XprojArgs& a, Tiles& tl, f32x16 
   load_x(a, b, t0, ka, XL);
   const int nch = a.D - kn < KC ? (int)(a.D - kn) : KC;
   step_products(acc, tl.u[P], tl.w[P], tb, mset, XN, head, a.conv0 != nullptr, nch, tl.c[P ^ 1], tl.u[P ^ 1]);
-  store_w(a, kn, m0, W, tl.w[P ^ 1]);
+  store_w(a, kn, W, tl.w[P ^ 1]);
   store_cw(a, ka, W, tl.c[P]);
   __syncthreads();
 }
@@ -316,7 +323,7 @@ __device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, f32x16 
   load_cw(a, 0, W);
   load_x(a, b, t0, 0, X0);
   load_x(a, b, t0, nsteps > 1 ? KC : 0, X1);
-  store_w(a, 0, m0, W, tl.w[0]);
+  store_w(a, 0, W, tl.w[0]);
   store_cw(a, 0, W, tl.c[0]);
   if (nsteps > 1) {
     load_cw(a, KC, W);
