@@ -14,9 +14,10 @@
 //     arithmetic, in the same order, of the conv front kernel, rounds it to bf16 (nearest
 //     even) and writes it transposed, [token][channel]; the 32 lanes of a half-wave take 32
 //     channels of one token group, so these 2-byte writes fill distinct banks.  Each lane
-//     reads its own channel row (one 16-byte load plus the 8 bytes before it for the conv
-//     history), so x is read with plain global loads: a buffer view needs one base per wave;
-//   - the W rows of the step's 64 channels are staged as they are, [row][channel];
+//     reads its own channel row (one 16-byte load through a buffer view of the step's 64 rows,
+//     plus the 12 bytes before it, or the cache at a row's start, for the conv history);
+//   - the W rows of the step's 64 channels are staged as they are, [row][channel], by loads that
+//     write LDS directly (no registers, no stores);
 //   - wave w multiplies its 32-token block (w & 3) by the row blocks w >> 2, w >> 2 + 2, ... of
 //     32 rows on the matrix cores: v_mfma_f32_32x32x16_bf16, fp32 accumulation, four per row
 //     block per step.  Operand fragments are 16-byte LDS reads: lane l takes row l % 32 and
@@ -26,13 +27,13 @@
 // The steps are software-pipelined so that the loads, the conv front and the products of
 // different steps overlap instead of running in turn:
 //   - x (with its conv weights) is loaded two steps ahead into one of two register sets, W one
-//     step ahead;
+//     step ahead straight into the other W tile;
 //   - while a wave multiplies step s, it computes u of step s + 1 into the other u tile, a
 //     quarter after each of the four 16-channel slices of products (the matrix cores run a
-//     product while the vector units compute), then stores step s + 1's W into the other W
-//     tile; one barrier per step.
-// Loads are unconditional (indices clamped into the tensors; u past D and W past D are zeroed
-// where they are consumed or stored), so no lane branches around a load.  The sums are rounded to bf16 (nearest even) once,
+//     product while the vector units compute); one barrier per step.
+// Loads are unconditional (indices clamped into the tensors; u past D is zeroed where it is
+// made, and W past D or M holds copies of in-range weights that meet u = 0 or feed dropped
+// rows), so no lane branches around a load.  The sums are rounded to bf16 (nearest even) once,
 // at the end, staged through LDS and written as whole 16-byte pieces of the output rows.
 #include <string.h>
 
@@ -49,11 +50,12 @@ constexpr int THREADS = WAVES * 64;
 constexpr int MB = 10;                     // row blocks of 32 per workgroup (320 rows)
 constexpr int ROWS = MB * 32;
 constexpr int PITCH = KC + 8;              // bf16 per LDS row (144 bytes)
-constexpr int WCHUNKS = ROWS * KC / 8;     // 16-byte chunks of a W step tile
-constexpr int WPT = WCHUNKS / THREADS;     // chunks per thread
+constexpr int WROW_SLOTS = PITCH * 2 / 16;  // 16-byte slots per W tile row: 8 of data, 1 of padding
+constexpr int WPT = (ROWS * WROW_SLOTS + THREADS - 1) / THREADS;  // slots each thread loads per step
+constexpr int WSLOTS = WPT * THREADS;         // slots per W tile (the last ones past the rows are spare)
 constexpr int MB_PER_WAVE = MB / 2;        // row blocks per wave (two row-block sets)
 constexpr int OPITCH = ROWS + 8;           // bf16 per token row of the output staging tile
-static_assert(WCHUNKS % THREADS == 0, "W tile chunks must divide among the threads");
+static_assert(WROW_SLOTS * 16 == PITCH * 2, "a W tile row is a whole number of 16-byte slots");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -76,12 +78,19 @@ struct XprojArgs {
   int M, R, N;
 };
 
+// The W tile of one step ([ROWS][PITCH] rows, then spare slots).  The two W tiles are separate
+// LDS objects, so that the compiler can tell the tile being filled from memory apart from the one
+// being read: it waits for the fill only where the filled tile is read (a single object of two
+// tiles made it wait at the first fragment read of every step).
+struct WTile {
+  uint16_t w[WSLOTS * 8];
+};
 struct Tiles {
   uint16_t u[2][TT * PITCH];
-  uint16_t w[2][ROWS * PITCH];
   float c[2][5 * KC];  // conv weights of a step: [KC] float4 taps, then [KC] biases
 };
-static_assert(sizeof(uint16_t) * TT * OPITCH <= sizeof(Tiles), "output staging must fit in the tiles");
+constexpr int HALF_TT = TT / 2;
+static_assert(sizeof(uint16_t) * HALF_TT * OPITCH <= sizeof(WTile), "half the output staging must fit in a W tile");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -97,10 +106,8 @@ struct XRegs {
   u32x3 xh[CPT];
 };
 
-// One thread's WPT 16-byte chunks of one step's W tile, and the conv taps and bias of one
-// channel of the step after it.
+// The conv taps and bias of one channel of a step, on their way to LDS.
 struct WRegs {
-  u32x4 wv[WPT];
   u32x4 cv;
   uint32_t cb;
 };
@@ -134,19 +141,27 @@ __device__ __forceinline__ void load_x(const XprojArgs& a, int64_t b, int64_t t0
   }
 }
 
-// W chunks of step k0 (rows m0 ..), read from clamped places past M or D (see store_w).
-__device__ __forceinline__ void load_w(const XprojArgs& a, int64_t k0, int m0, WRegs& r) {
+// W of step k0 (rows m0 ..) straight from memory into the tile wt (16-byte loads that write LDS
+// directly: lane i of a wave's load fills slot base + i).  Slot j of the tile is row j / 9, chunk
+// j % 9 (chunk 8 is the row's padding, and slots past the last row are spare: both take a copy of
+// an in-range chunk).  Reads are clamped into W: rows past M hold copies of row M - 1 and feed only
+// output rows that are never stored; chunks past D hold copies of in-range weights, multiplied by
+// u = 0 there.
+__device__ __forceinline__ void dma_w(const XprojArgs& a, int64_t k0, int m0, uint16_t* wt) {
   // 32-bit offsets: the caller keeps W below 2 GiB
   const auto rw = rsrc(a.w, (int64_t)a.M * a.D * 2);
   const int D = (int)a.D, k = (int)k0;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
-    const int ci = threadIdx.x + i * THREADS;  // chunk: row ci / (KC / 8), channels 8 (ci % (KC / 8)) ..
-    const int row = m0 + ci / (KC / 8);
-    const int kq = k + 8 * (ci % (KC / 8));
-    const int rr = row < a.M ? row : a.M - 1;
+    const int base = i * THREADS + 64 * wave;  // the wave's first slot (uniform)
+    const int slot = base + lane;
+    const int row = slot / WROW_SLOTS, q = slot - row * WROW_SLOTS;
+    const int rr = m0 + row < a.M ? m0 + row : a.M - 1;
+    const int kq = k + 8 * (q < 8 ? q : 7);
     const int kk = kq < D ? kq : D - 8;
-    r.wv[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (rr * D + kk) * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(wt + base * 8), 16,
+                                             (rr * D + kk) * 2, 0, 0, 0);
   }
 }
 
@@ -160,22 +175,6 @@ __device__ __forceinline__ void load_cw(const XprojArgs& a, int64_t kc, WRegs& r
   r.cv = __builtin_amdgcn_raw_buffer_load_b128(rw, ii * 16, 0, 0);
   const auto rb = a.conv_b ? rsrc(a.conv_b + kc, (int64_t)(last + 1) * 4) : rw;
   r.cb = __builtin_amdgcn_raw_buffer_load_b32(rb, ii * 4, 0, 0);
-}
-
-// Rows past M hold copies of row M - 1 (clamped reads): they feed only output rows past M, which
-// are never stored.  Channels past D are zeroed (the step that reaches past D only; a uniform
-// branch), so that they add nothing to the rows that are stored.
-__device__ __forceinline__ void store_w(const XprojArgs& a, int64_t k0, const WRegs& r, uint16_t* wt) {
-  const bool full = k0 + KC <= a.D;
-#pragma unroll
-  for (int i = 0; i < WPT; ++i) {
-    const int ci = threadIdx.x + i * THREADS;
-    u32x4* dst = reinterpret_cast<u32x4*>(&wt[(ci / (KC / 8)) * PITCH + 8 * (ci % (KC / 8))]);
-    if (full)
-      *dst = r.wv[i];
-    else
-      *dst = k0 + 8 * (ci % (KC / 8)) < a.D ? r.wv[i] : u32x4{0u, 0u, 0u, 0u};
-  }
 }
 
 // Threads 0 .. KC - 1 store their channel's taps and bias ([KC] float4, then [KC] float).
@@ -295,35 +294,35 @@ __device__ __forceinline__ void step_products(f32x16 (&acc)[MB_PER_WAVE], const 
 // step s + 2 into XL.  All of it runs in every step, past the last step on repeated data into
 // tiles that are no longer read: no load or wait then depends on a branch.
 template <int P>
-__device__ __forceinline__ void pipe_step(const XprojArgs& a, Tiles& tl, f32x16 (&acc)[MB_PER_WAVE], int64_t b,
+__device__ __forceinline__ void pipe_step(const XprojArgs& a, Tiles& tl, WTile& w0, WTile& w1,
+                                          f32x16 (&acc)[MB_PER_WAVE], int64_t b,
                                           int64_t t0, int m0, int tb, int mset, bool head, int s, int nsteps,
                                           WRegs& W, XRegs& XL, const XRegs& XN) {
   const bool next = s + 1 < nsteps, after = s + 2 < nsteps;
   const int64_t kn = (int64_t)(next ? s + 1 : s) * KC;
   const int64_t ka = (int64_t)(after ? s + 2 : nsteps - 1) * KC;
   // issue order: what this step stores at its end first, x last (its wait is two steps away)
-  load_w(a, kn, m0, W);
+  dma_w(a, kn, m0, P ? w0.w : w1.w);
   load_cw(a, ka, W);
   load_x(a, b, t0, ka, XL);
   const int nch = a.D - kn < KC ? (int)(a.D - kn) : KC;
-  step_products(acc, tl.u[P], tl.w[P], tb, mset, XN, head, a.conv0 != nullptr, nch, tl.c[P ^ 1], tl.u[P ^ 1]);
-  store_w(a, kn, W, tl.w[P ^ 1]);
+  step_products(acc, tl.u[P], P ? w1.w : w0.w, tb, mset, XN, head, a.conv0 != nullptr, nch, tl.c[P ^ 1], tl.u[P ^ 1]);
   store_cw(a, ka, W, tl.c[P]);
   __syncthreads();
 }
 
-__device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, f32x16 (&acc)[MB_PER_WAVE], int64_t b,
+__device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, WTile& w0, WTile& w1,
+                                          f32x16 (&acc)[MB_PER_WAVE], int64_t b,
                                           int64_t t0, int m0, int tb, int mset) {
   const int nsteps = (int)((a.D + KC - 1) / KC);
   const bool head = t0 == 0 && (threadIdx.x >> 5) == 0;  // this thread's group starts a row
   const bool cache = a.conv0 != nullptr;
   XRegs X0, X1;
   WRegs W;
-  load_w(a, 0, m0, W);
+  dma_w(a, 0, m0, w0.w);
   load_cw(a, 0, W);
   load_x(a, b, t0, 0, X0);
   load_x(a, b, t0, nsteps > 1 ? KC : 0, X1);
-  store_w(a, 0, W, tl.w[0]);
   store_cw(a, 0, W, tl.c[0]);
   if (nsteps > 1) {
     load_cw(a, KC, W);
@@ -340,25 +339,26 @@ __device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, f32x16 
   // Two steps per trip, so that each register set and tile has a fixed role in each half.
   int s = 0;
   for (; s + 1 < nsteps; s += 2) {
-    pipe_step<0>(a, tl, acc, b, t0, m0, tb, mset, head, s, nsteps, W, X0, X1);
-    pipe_step<1>(a, tl, acc, b, t0, m0, tb, mset, head, s + 1, nsteps, W, X1, X0);
+    pipe_step<0>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, W, X0, X1);
+    pipe_step<1>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s + 1, nsteps, W, X1, X0);
   }
-  if (s < nsteps) pipe_step<0>(a, tl, acc, b, t0, m0, tb, mset, head, s, nsteps, W, X0, X1);
+  if (s < nsteps) pipe_step<0>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, W, X0, X1);
 }
 
 // Copy rows [lo, hi) of the stacked output (tensor `out`, width hi - lo) held in the staging
-// tile for this workgroup's ntok tokens: V = 8 moves whole 16-byte pieces (each token's run
-// starts 16-byte aligned and is a multiple of 8 long), V = 1 single elements.
+// tiles for this workgroup's ntok tokens (tokens 0..63 in ot0, 64..127 in ot1): V = 8 moves whole
+// 16-byte pieces (each token's run starts 16-byte aligned and is a multiple of 8 long), V = 1
+// single elements.
 template <int V>
-__device__ __forceinline__ void copy_rows(const uint16_t* ot, uint16_t* out, int64_t tok0, int ntok, int m0, int lo,
-                                          int hi) {
+__device__ __forceinline__ void copy_rows(const uint16_t* ot0, const uint16_t* ot1, uint16_t* out, int64_t tok0,
+                                          int ntok, int m0, int lo, int hi) {
   const int a0 = lo > m0 ? lo : m0, a1 = hi < m0 + ROWS ? hi : m0 + ROWS;
   if (a0 >= a1) return;
   const int width = hi - lo, run = (a1 - a0) / V;
   const int total = ntok * run;
   for (int e = threadIdx.x; e < total; e += THREADS) {
     const int tok = e / run, col = V * (e - tok * run);
-    const uint16_t* src = &ot[tok * OPITCH + (a0 - m0) + col];
+    const uint16_t* src = &(tok < HALF_TT ? ot0 : ot1)[(tok % HALF_TT) * OPITCH + (a0 - m0) + col];
     uint16_t* dst = out + (tok0 + tok) * width + (a0 - lo) + col;
     if (V == 8)
       *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
@@ -375,6 +375,8 @@ __device__ __forceinline__ bool vec_ok(const void* out, int m0, int lo, int hi) 
 
 __global__ __launch_bounds__(THREADS) void conv_xproj_kernel(XprojArgs a) {
   __shared__ __attribute__((aligned(16))) Tiles tl;
+  __shared__ __attribute__((aligned(16))) WTile w0;
+  __shared__ __attribute__((aligned(16))) WTile w1;
   const int64_t tiles_per_row = (a.L + TT - 1) / TT;
   const int64_t b = blockIdx.x / tiles_per_row;
   const int64_t t0 = (blockIdx.x - b * tiles_per_row) * TT;
@@ -386,13 +388,14 @@ __global__ __launch_bounds__(THREADS) void conv_xproj_kernel(XprojArgs a) {
   f32x16 acc[MB_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < MB_PER_WAVE; ++i) acc[i] = f32x16{};
-  main_loop(a, tl, acc, b, t0, m0, tb, mset);
+  main_loop(a, tl, w0, w1, acc, b, t0, m0, tb, mset);
 
-  // Stage the sums, rounded to bf16, as [token][row] (the last barrier of the loop has freed
-  // the tiles): acc[i] register j is row 32 blk + 8 (j / 4) + 4 (lane / 32) + j % 4 of token
-  // 32 tb + lane % 32, and registers j, j + 1 are adjacent rows.
-  uint16_t* ot = reinterpret_cast<uint16_t*>(&tl);
-  const int tok = 32 * tb + (lane & 31);
+  // Stage the sums, rounded to bf16, as [token][row] in the W tiles (the last barrier of the loop
+  // has freed them; tokens 0..63 in w0, 64..127 in w1): acc[i] register j is row
+  // 32 blk + 8 (j / 4) + 4 (lane / 32) + j % 4 of token 32 tb + lane % 32, and registers j, j + 1
+  // are adjacent rows.
+  uint16_t* ot = tb < 2 ? w0.w : w1.w;  // uniform over the wave
+  const int tok = 32 * (tb & 1) + (lane & 31);
 #pragma unroll
   for (int i = 0; i < MB_PER_WAVE; ++i) {
     const int blk = mset + 2 * i;
@@ -412,9 +415,9 @@ __global__ __launch_bounds__(THREADS) void conv_xproj_kernel(XprojArgs a) {
 #pragma unroll
   for (int o = 0; o < 3; ++o) {
     if (vec_ok(outs[o], m0, lo[o], hi[o]))
-      copy_rows<8>(ot, outs[o], tok0, ntok, m0, lo[o], hi[o]);
+      copy_rows<8>(w0.w, w1.w, outs[o], tok0, ntok, m0, lo[o], hi[o]);
     else
-      copy_rows<1>(ot, outs[o], tok0, ntok, m0, lo[o], hi[o]);
+      copy_rows<1>(w0.w, w1.w, outs[o], tok0, ntok, m0, lo[o], hi[o]);
   }
 }
 
