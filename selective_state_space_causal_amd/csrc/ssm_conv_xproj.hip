@@ -145,23 +145,40 @@ __device__ __forceinline__ void load_x(const XprojArgs& a, int64_t b, int64_t t0
 // directly: lane i of a wave's load fills slot base + i).  Slot j of the tile is row j / 9, chunk
 // j % 9 (chunk 8 is the row's padding, and slots past the last row are spare: both take a copy of
 // an in-range chunk).  Reads are clamped into W: rows past M hold copies of row M - 1 and feed only
-// output rows that are never stored; chunks past D hold copies of in-range weights, multiplied by
-// u = 0 there.
-__device__ __forceinline__ void dma_w(const XprojArgs& a, int64_t k0, int m0, uint16_t* wt) {
-  // 32-bit offsets: the caller keeps W below 2 GiB
-  const auto rw = rsrc(a.w, (int64_t)a.M * a.D * 2);
-  const int D = (int)a.D, k = (int)k0;
+// output rows that are never stored; chunks past D hold copies of the row's last in-range chunk,
+// multiplied by u = 0 there.  A slot's byte offset is its row's and chunk's part (the same in every
+// step, computed once: WSlots) plus 2 k0, capped at its row's last chunk: one add and one min per
+// slot and step, with no branch (a branch between a fast and a clamped form made the compiler
+// wait for this step's W before the conv front's first use of x).
+struct WSlots {
+  int off[WPT];  // (row * D + 8 * chunk) * 2 of this thread's slots, chunk 8 taken as 7
+  int lim[WPT];  // (row * D + D - 8) * 2: the row's last in-range chunk
+};
+
+__device__ __forceinline__ WSlots w_slots(const XprojArgs& a, int m0) {
+  WSlots ws;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
-    const int base = i * THREADS + 64 * wave;  // the wave's first slot (uniform)
-    const int slot = base + lane;
+    const int slot = i * THREADS + 64 * wave + lane;
     const int row = slot / WROW_SLOTS, q = slot - row * WROW_SLOTS;
     const int rr = m0 + row < a.M ? m0 + row : a.M - 1;
-    const int kq = k + 8 * (q < 8 ? q : 7);
-    const int kk = kq < D ? kq : D - 8;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(wt + base * 8), 16,
-                                             (rr * D + kk) * 2, 0, 0, 0);
+    ws.off[i] = (rr * (int)a.D + 8 * (q < 8 ? q : 7)) * 2;
+    ws.lim[i] = (rr * (int)a.D + (int)a.D - 8) * 2;
+  }
+  return ws;
+}
+
+__device__ __forceinline__ void dma_w(const XprojArgs& a, int64_t k0, const WSlots& ws, uint16_t* wt) {
+  // 32-bit offsets: the caller keeps W below 2 GiB
+  const auto rw = rsrc(a.w, (int64_t)a.M * a.D * 2);
+  const int k2 = 2 * (int)k0;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int o = ws.off[i] + k2 < ws.lim[i] ? ws.off[i] + k2 : ws.lim[i];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(wt + (i * THREADS + 64 * wave) * 8),
+                                             16, o, 0, 0, 0);
   }
 }
 
@@ -297,12 +314,12 @@ template <int P>
 __device__ __forceinline__ void pipe_step(const XprojArgs& a, Tiles& tl, WTile& w0, WTile& w1,
                                           f32x16 (&acc)[MB_PER_WAVE], int64_t b,
                                           int64_t t0, int m0, int tb, int mset, bool head, int s, int nsteps,
-                                          WRegs& W, XRegs& XL, const XRegs& XN) {
+                                          const WSlots& ws, WRegs& W, XRegs& XL, const XRegs& XN) {
   const bool next = s + 1 < nsteps, after = s + 2 < nsteps;
   const int64_t kn = (int64_t)(next ? s + 1 : s) * KC;
   const int64_t ka = (int64_t)(after ? s + 2 : nsteps - 1) * KC;
   // issue order: what this step stores at its end first, x last (its wait is two steps away)
-  dma_w(a, kn, m0, P ? w0.w : w1.w);
+  dma_w(a, kn, ws, P ? w0.w : w1.w);
   load_cw(a, ka, W);
   load_x(a, b, t0, ka, XL);
   const int nch = a.D - kn < KC ? (int)(a.D - kn) : KC;
@@ -319,7 +336,8 @@ __device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, WTile& 
   const bool cache = a.conv0 != nullptr;
   XRegs X0, X1;
   WRegs W;
-  dma_w(a, 0, m0, w0.w);
+  const WSlots ws = w_slots(a, m0);
+  dma_w(a, 0, ws, w0.w);
   load_cw(a, 0, W);
   load_x(a, b, t0, 0, X0);
   load_x(a, b, t0, nsteps > 1 ? KC : 0, X1);
@@ -339,10 +357,10 @@ __device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, WTile& 
   // Two steps per trip, so that each register set and tile has a fixed role in each half.
   int s = 0;
   for (; s + 1 < nsteps; s += 2) {
-    pipe_step<0>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, W, X0, X1);
-    pipe_step<1>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s + 1, nsteps, W, X1, X0);
+    pipe_step<0>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, ws, W, X0, X1);
+    pipe_step<1>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s + 1, nsteps, ws, W, X1, X0);
   }
-  if (s < nsteps) pipe_step<0>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, W, X0, X1);
+  if (s < nsteps) pipe_step<0>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, ws, W, X0, X1);
 }
 
 // Copy rows [lo, hi) of the stacked output (tensor `out`, width hi - lo) held in the staging
