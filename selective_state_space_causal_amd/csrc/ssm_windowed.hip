@@ -227,6 +227,10 @@ __device__ __forceinline__ void tile_states(const float* p, float (&v)[G]) {
   }
 }
 
+// A scheduling fence for LDS reads only: the tile reads issued before it stay before the
+// arithmetic after it (vector and scalar ALU work may still move across it).
+__device__ __forceinline__ void keep_lds_reads_here() { __builtin_amdgcn_sched_barrier(0x6); }
+
 __device__ __forceinline__ float lane63(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
     hist2 = lane63(xv[K - 1]);
 
     float dl[K], du[K], yv[K];
-    float dsum = 0.0f;
+    float dsum;
     // Past the row end the step is the identity: delta is exactly 0 (softplus(-inf)) and so is
     // the drive delta * u, selected rather than multiplied, since u there is made of whatever
     // the tensors hold past the row (NaN and infinities included).  The tile's B there is
@@ -525,7 +529,7 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
         dl[j] = d;
         du[j] = pad ? 0.0f : d * u;
         yv[j] = dsk * u;
-        dsum += d;
+        dsum = j == 0 ? d : dsum + d;
       }
     };
     // With two waves per SIMD (8-state groups) the front end, too, runs at raised priority:
@@ -542,26 +546,40 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
     for (int q0 = 0; q0 < NS; q0 += G) {
       float av[K][G], bv[K][G], P[G], H[G];
 #pragma unroll
-      for (int q = 0; q < G; ++q) {
-        P[q] = hw_exp2(A2[q0 + q] * dsum);  // prod_j exp(delta_j A) over this lane's tokens
-        H[q] = 0.0f;
-      }
+      for (int q = 0; q < G; ++q) P[q] = hw_exp2(A2[q0 + q] * dsum);  // prod_j exp(delta_j A) over this lane's tokens
       float hc[G], cg[G];
 #pragma unroll
       for (int q = 0; q < G; ++q) cg[q] = carry[q0 + q];
+      // The fold reads each token's B one token ahead (bn), and orders the token's work as: the
+      // next token's tile read, the decay arguments of all G states, then their exponentials,
+      // the drives and the pair updates.  Each tile read then has a token's work before its
+      // first use, and no exponential waits on the multiply just before it (against reading
+      // and using in the same token: 375 -> 359 us on slice7b, with the replay's read-ahead below).
+      float bn[G];
+      tile_states<G>(tb + q0, bn);
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         float bq[G];
-        tile_states<G>(tb + j * NS + q0, bq);
+#pragma unroll
+        for (int q = 0; q < G; ++q) bq[q] = bn[q];
+        if (j + 1 < K) tile_states<G>(tb + (j + 1) * NS + q0, bn);
+        keep_lds_reads_here();
+#pragma unroll
+        for (int q = 0; q < G; ++q) av[j][q] = dl[j] * A2[q0 + q];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < G; ++q) {
-          av[j][q] = hw_exp2(dl[j] * A2[q0 + q]);
+          av[j][q] = hw_exp2(av[j][q]);
           bv[j][q] = du[j] * bq[q];
         }
         if (j == 0) seed_carry<G>(bv[0], av[0], cg);
+        // The first token's pair is its own drive (the state reached from zero).
 #pragma unroll
-        for (int q = 0; q < G; ++q) H[q] = fmaf(av[j][q], H[q], bv[j][q]);
+        for (int q = 0; q < G; ++q) H[q] = j == 0 ? bv[0][q] : fmaf(av[j][q], H[q], bv[j][q]);
       }
+      // The replay's first C read goes out before the lane scan, which hides its latency.
+      float cn[G];
+      tile_states<G>(tcp + q0, cn);
       // The lane scan is a chain of dependent DPP steps; raising the wave's issue priority for it
       // lets the other waves of the SIMD fill the gaps with their (independent) fold and replay
       // work instead of the reverse (3-4% faster with three or four waves per SIMD).
@@ -573,7 +591,10 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         float cq[G];
-        tile_states<G>(tcp + j * NS + q0, cq);
+#pragma unroll
+        for (int q = 0; q < G; ++q) cq[q] = cn[q];
+        if (j + 1 < K) tile_states<G>(tcp + (j + 1) * NS + q0, cn);
+        keep_lds_reads_here();
 #pragma unroll
         for (int q = 0; q < G; ++q) {
           hc[q] = fmaf(av[j][q], hc[q], bv[j][q]);
