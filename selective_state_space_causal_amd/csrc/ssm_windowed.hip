@@ -36,7 +36,7 @@ constexpr int WIN = WAVE * K;       // tokens per window
 // operations in the same order -- so every shape gives bit-identical results, and the choice
 // may follow the channel count.  A workgroup of any shape fills one CU (registers and the
 // two LDS tiles), so a launch runs in rounds of one workgroup per CU:
-//   W 8,  G 8: two waves per SIMD, eight independent state chains per pass; 248 VGPRs;
+//   W 8,  G 8: two waves per SIMD, eight independent state chains per pass; 249 VGPRs;
 //   W 12, G 4: three waves per SIMD; 168 VGPRs; a round takes ~1.40x as long as W 8's for
 //              1.5x the channels;
 //   W 16, G 2: four waves per SIMD; at most 128 VGPRs; a round ~1.84x W 8's for 2x the channels;
@@ -550,13 +550,31 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
       float hc[G], cg[G];
 #pragma unroll
       for (int q = 0; q < G; ++q) cg[q] = carry[q0 + q];
-      // The fold reads each token's B one token ahead (bn), and orders the token's work as: the
-      // next token's tile read, the decay arguments of all G states, then their exponentials,
-      // the drives and the pair updates.  Each tile read then has a token's work before its
-      // first use, and no exponential waits on the multiply just before it (against reading
-      // and using in the same token: 375 -> 359 us on slice7b, with the replay's read-ahead below).
+      // The fold reads each token's B one token ahead (bn), so that each tile read has a token's
+      // work before its first use, and computes each decay's argument before its exponential,
+      // so that no exponential waits on the multiply just before it (against reading and using
+      // in the same token: 375 -> 359 us on slice7b, with the replay's read-ahead below).  With
+      // 8-state groups (two waves per SIMD, which reach the fold together) or 2-state groups,
+      // all arguments of the group come first (after its first B read), then all its exponentials,
+      // then the drives and pair updates token by token: the two waves' transcendentals run back
+      // to back and their plain work pairs up afterwards (slice7b 359 -> 350 us, 16-channel shape
+      // -1%); with 4-state groups that ordering was 0.3-1% slower, so the arguments and
+      // exponentials stay with their token there.
+      constexpr bool kExpBurst = G != 4;
       float bn[G];
       tile_states<G>(tb + q0, bn);
+      if constexpr (kExpBurst) {
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+#pragma unroll
+          for (int q = 0; q < G; ++q) av[j][q] = dl[j] * A2[q0 + q];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+#pragma unroll
+          for (int q = 0; q < G; ++q) av[j][q] = hw_exp2(av[j][q]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         float bq[G];
@@ -564,12 +582,14 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
         for (int q = 0; q < G; ++q) bq[q] = bn[q];
         if (j + 1 < K) tile_states<G>(tb + (j + 1) * NS + q0, bn);
         keep_lds_reads_here();
+        if constexpr (!kExpBurst) {
 #pragma unroll
-        for (int q = 0; q < G; ++q) av[j][q] = dl[j] * A2[q0 + q];
-        __builtin_amdgcn_sched_barrier(0);
+          for (int q = 0; q < G; ++q) av[j][q] = dl[j] * A2[q0 + q];
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int q = 0; q < G; ++q) {
-          av[j][q] = hw_exp2(av[j][q]);
+          if constexpr (!kExpBurst) av[j][q] = hw_exp2(av[j][q]);
           bv[j][q] = du[j] * bq[q];
         }
         if (j == 0) seed_carry<G>(bv[0], av[0], cg);
