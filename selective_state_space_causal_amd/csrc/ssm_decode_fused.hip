@@ -5,10 +5,10 @@
 //
 // x_proj contracts over every channel of the slice, and dt_proj and the step of every channel
 // need its result, so the work splits at that reduction:
-//   xproj_partial  one workgroup per (batch row, block of 64 channels): the block's conv front
-//                  from the cache (rounded to the io dtype, as the unfused layer stores u), then
-//                  the block's share of each of the R + 2N x_proj outputs, one output per
-//                  thread, written as an fp32 partial sum into the workspace;
+//   xproj_partial  one workgroup per (batch row, block of 64 channels, block of 64 outputs): the
+//                  block's conv front from the cache (rounded to the io dtype, as the unfused layer
+//                  stores u), then the channel block's share of 64 of the R + 2N x_proj outputs,
+//                  four threads per output, written as an fp32 partial sum into the workspace;
 //   dt_decode      one workgroup per (batch row, block of 64 channels), four lanes per channel:
 //                  the batch row's R + 2N outputs as the sum of the blocks' partials (in block
 //                  order, then rounded to the io dtype), then per channel its dt_proj dot product
@@ -68,36 +68,40 @@ __device__ __forceinline__ void load8(const IO* p, float (&v)[8]) {
   }
 }
 
-// Outputs per thread of xproj_partial: R + 2N <= 512 rows over 256 threads.
-constexpr int kRowsPerThread = (kMaxRows + kThreads - 1) / kThreads;
+// xproj_partial: a workgroup takes one batch row's block of 64 channels and 64 of the M rows,
+// four threads per row (16 channels each; the four sums added across the quad), so that a call
+// runs B x ceil(D / 64) x ceil(M / 64) workgroups of short loads (the 7B-class slice: 160; with
+// one workgroup per channel block and one thread per row, 32 workgroups, 0.8 us slower per token).
+constexpr int kRowsPerWG = kThreads / 4;
+constexpr int kQuarter = kCB / 4;  // channels per thread
 
-// VEC: D is a multiple of 8 and w_x 16-byte aligned, so a block's row segment is whole 16-byte
-// pieces.  Every global load is issued before the first barrier: each thread's weight segments
-// (one per output row it owns) and, on the first 64 threads, the conv front's inputs.
+// VEC: D is a multiple of 8 and w_x 16-byte aligned, so a quarter row is whole 16-byte pieces.
+// Every global load is issued before the barrier: the thread's two weight pieces and, on the
+// first 64 threads, the conv front's inputs.
 template <typename IO, bool VEC>
 __global__ __launch_bounds__(kThreads) void xproj_partial(FusedArgs a) {
   __shared__ float us[kCB];
-  const int64_t b = blockIdx.x / a.nblk;
-  const int blk = (int)(blockIdx.x - b * a.nblk);
+  const int nrb = (a.M + kRowsPerWG - 1) / kRowsPerWG;
+  const int rb = (int)(blockIdx.x % (unsigned)nrb);
+  const int64_t bb = blockIdx.x / (unsigned)nrb;
+  const int64_t b = bb / a.nblk;
+  const int blk = (int)(bb - b * a.nblk);
   const int t = threadIdx.x;
+  const int r = rb * kRowsPerWG + (t >> 2), k = t & 3;
+  const int rc = r < a.M ? r : a.M - 1;  // rows past M repeat the last one and store nothing
   const int64_t c0 = (int64_t)blk * kCB;
   const int ncb = (int)min((int64_t)kCB, a.D - c0);
   const bool full = VEC && ncb == kCB;
-  // This thread's rows' segments (full blocks only) as raw 16-byte pieces, unpacked only where
-  // they are used (after the barrier), so that their loads stay in flight with the conv front's.
+  // The quarter row as raw 16-byte pieces, unpacked only after the barrier, so that the loads
+  // stay in flight with the conv front's.
   constexpr int kPer = 16 / (int)sizeof(IO);
-  constexpr int kPieces = kCB / kPer;
-  u32x4 wraw[kRowsPerThread][kPieces];
+  constexpr int kQP = kQuarter / kPer;
+  u32x4 wraw[kQP];
   if (full) {
+    const u32x4* wp =
+        reinterpret_cast<const u32x4*>(static_cast<const IO*>(a.wx) + (int64_t)rc * a.D + c0 + kQuarter * k);
 #pragma unroll
-    for (int k = 0; k < kRowsPerThread; ++k) {
-      const int j = t + k * kThreads;
-      if (j < a.M) {
-        const u32x4* wp = reinterpret_cast<const u32x4*>(static_cast<const IO*>(a.wx) + (int64_t)j * a.D + c0);
-#pragma unroll
-        for (int i = 0; i < kPieces; ++i) wraw[k][i] = wp[i];
-      }
-    }
+    for (int i = 0; i < kQP; ++i) wraw[i] = wp[i];
   }
   if (t < kCB) {
     float u = 0.0f;
@@ -114,34 +118,32 @@ __global__ __launch_bounds__(kThreads) void xproj_partial(FusedArgs a) {
     us[t] = u;
   }
   __syncthreads();
+  float acc = 0.0f;
+  if (full) {
 #pragma unroll
-  for (int k = 0; k < kRowsPerThread; ++k) {
-    const int j = t + k * kThreads;
-    if (j >= a.M) break;
-    float acc = 0.0f;
-    if (full) {
+    for (int i = 0; i < kQP; ++i) {
+      float v[kPer];
+      if constexpr (sizeof(IO) == 2) {
 #pragma unroll
-      for (int i = 0; i < kPieces; ++i) {
-        float v[kPer];
-        if constexpr (sizeof(IO) == 2) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[2 * e] = __uint_as_float(wraw[k][i][e] << 16);
-            v[2 * e + 1] = __uint_as_float(wraw[k][i][e] & 0xFFFF0000u);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(wraw[k][i][e]);
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = __uint_as_float(wraw[i][e] << 16);
+          v[2 * e + 1] = __uint_as_float(wraw[i][e] & 0xFFFF0000u);
         }
+      } else {
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) acc = fmaf(v[e], us[kPer * i + e], acc);
+        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(wraw[i][e]);
       }
-    } else {
-      const IO* wr = static_cast<const IO*>(a.wx) + (int64_t)j * a.D + c0;
-      for (int i = 0; i < ncb; ++i) acc = fmaf(to_f32(wr[i]), us[i], acc);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc = fmaf(v[e], us[kQuarter * k + kPer * i + e], acc);
     }
-    a.part[((int64_t)b * a.nblk + blk) * a.M + j] = acc;
+  } else {
+    const IO* wr = static_cast<const IO*>(a.wx) + (int64_t)rc * a.D + c0;
+    const int hi = min(kQuarter * k + kQuarter, ncb);
+    for (int c = kQuarter * k; c < hi; ++c) acc = fmaf(to_f32(wr[c]), us[c], acc);
   }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  if (k == 0 && r < a.M) a.part[((int64_t)b * a.nblk + blk) * a.M + r] = acc;
 }
 
 constexpr int kPartBatch = 32;  // partial sums read together (one round trip for up to 2048 channels)
@@ -261,8 +263,9 @@ __global__ __launch_bounds__(kThreads) void dt_decode(FusedArgs a) {
 template <typename IO>
 hipError_t launch(const FusedArgs& a, bool vec_x, bool vec_dt, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.nblk)), block(kThreads);
-  if (vec_x) xproj_partial<IO, true><<<grid, block, 0, s>>>(a);
-  else xproj_partial<IO, false><<<grid, block, 0, s>>>(a);
+  const dim3 xgrid((unsigned)(a.B * a.nblk * ((a.M + kRowsPerWG - 1) / kRowsPerWG)));
+  if (vec_x) xproj_partial<IO, true><<<xgrid, block, 0, s>>>(a);
+  else xproj_partial<IO, false><<<xgrid, block, 0, s>>>(a);
   if (vec_dt) dt_decode<IO, true><<<grid, block, 0, s>>>(a);
   else dt_decode<IO, false><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
@@ -284,8 +287,9 @@ bool fused_sizes(const ssm_dims* d, int64_t rank, int64_t* nblk, int64_t* ws_byt
       d->d_conv != SSM_CONV_WIDTH || rank < 1 || rank + 2 * kNS > kMaxRows)
     return false;
   *nblk = (d->d_inner + kCB - 1) / kCB;
+  const int64_t nrb = (rank + 2 * kNS + kRowsPerWG - 1) / kRowsPerWG;  // x_proj row blocks
   int64_t t;
-  if (__builtin_mul_overflow(d->batch, *nblk, &t) || t >= ((int64_t)1 << 31) ||
+  if (__builtin_mul_overflow(d->batch, *nblk, &t) || t * nrb >= ((int64_t)1 << 31) ||
       __builtin_mul_overflow(t, (rank + 2 * kNS) * 4, ws_bytes) ||
       __builtin_mul_overflow(d->batch, d->d_inner * kNS * 4, &t))
     return false;
