@@ -480,16 +480,39 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
     // and every wave is done reading tiles[(w+1) & 1] (window w-1's), which is refilled below.
     __syncthreads();
     const Tile& tile = tiles[w & 1];
-    const Lanes<IO, ALIGNED> cx = px, cdt = pdt, cz = pz;
+    // The next window's inputs are prefetched while this one is computed.  With two waves per
+    // SIMD (8-wave workgroups) x, dt and z are loaded at the window's start, into a second set of
+    // registers; with three or four waves per SIMD x and dt are loaded right after the front end
+    // has consumed this window's, and z after the gate, into the same registers (12 fewer
+    // copies per window: 0.9-1.6% faster there, but 5% slower with two waves per SIMD, whose
+    // loads issued mid-window are not covered by other waves' work).  Past the last window the
+    // views are empty and those loads return zeros.
+    constexpr bool kLateLoads = W > 8;
     const bool more = w + 1 < nwin;
-    if (more) {  // prefetch the next window while this one is computed
-      const int t1 = t0 + WIN;
+    const int t1 = t0 + WIN;
+    Lanes<IO, ALIGNED> cx, cdt, cz;
+    if constexpr (!kLateLoads) {
+      cx = px;
+      cdt = pdt;
+      cz = pz;
+    }
+    const Lanes<IO, ALIGNED>& ux = kLateLoads ? px : cx;
+    const Lanes<IO, ALIGNED>& udt = kLateLoads ? pdt : cdt;
+    const Lanes<IO, ALIGNED>& uz = kLateLoads ? pz : cz;
+    if (more) {
       pf.fetch(window_rsrc(Brow, bc_elems, t1 * NS), window_rsrc(Crow, bc_elems, t1 * NS));
-      px.load(window_rsrc(xrow, Li, t1), voff);
-      pdt.load(window_rsrc(dtrow, Li, t1), voff);
-      if (gate) pz.load(window_rsrc(zrow, Li, t1), voff);
+      if constexpr (!kLateLoads) {
+        px.load(window_rsrc(xrow, Li, t1), voff);
+        pdt.load(window_rsrc(dtrow, Li, t1), voff);
+        if (gate) pz.load(window_rsrc(zrow, Li, t1), voff);
+      }
     }
     if (!active) {
+      if constexpr (kLateLoads) {
+        px.load(window_rsrc(xrow, Li, t1), voff);
+        pdt.load(window_rsrc(dtrow, Li, t1), voff);
+        if (gate) pz.load(window_rsrc(zrow, Li, t1), voff);
+      }
       if (more) pf.store(tiles[(w + 1) & 1]);
       continue;
     }
@@ -500,7 +523,7 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
     const int nvalid = rem - lane * K < 0 ? 0 : (rem - lane * K > K ? K : rem - lane * K);
     float xv[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) xv[j] = unpack<IO>(cx.w, j);
+    for (int j = 0; j < K; ++j) xv[j] = unpack<IO>(ux.w, j);
     const float xm3 = dpp<DPP_WAVE_SHR1, 0xf>(hist0, xv[K - 3]);
     const float xm2 = dpp<DPP_WAVE_SHR1, 0xf>(hist1, xv[K - 2]);
     const float xm1 = dpp<DPP_WAVE_SHR1, 0xf>(hist2, xv[K - 1]);
@@ -524,7 +547,7 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
         const float s1 = j >= 1 ? xv[j - 1] : xm1;
         const float v = fmaf(w3, xv[j], fmaf(w2, s1, fmaf(w1, s2, fmaf(w0, s3, cb))));
         const float u = silu(v);
-        const float arg = unpack<IO>(cdt.w, j) + dtb;
+        const float arg = unpack<IO>(udt.w, j) + dtb;
         const float d = softplus(pad ? -__builtin_inff() : arg);
         dl[j] = d;
         du[j] = pad ? 0.0f : d * u;
@@ -538,6 +561,10 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
     if (rem == WIN) front(std::integral_constant<bool, false>{});
     else front(std::integral_constant<bool, true>{});
     if constexpr (G == 8) __builtin_amdgcn_s_setprio(0);
+    if constexpr (kLateLoads) {
+      px.load(window_rsrc(xrow, Li, t1), voff);
+      pdt.load(window_rsrc(dtrow, Li, t1), voff);
+    }
 
     // ---- state groups: local pairs, lane scan, replay ----
     const float* tb = &tile.B[lane * LANE_STRIDE];
@@ -625,7 +652,10 @@ __global__ __launch_bounds__(W * WAVE) void prefill_windowed(ScanArgs a) {
 
     if (gate) {
 #pragma unroll
-      for (int j = 0; j < K; ++j) yv[j] *= silu(unpack<IO>(cz.w, j));
+      for (int j = 0; j < K; ++j) yv[j] *= silu(unpack<IO>(uz.w, j));
+    }
+    if constexpr (kLateLoads) {
+      if (gate) pz.load(window_rsrc(zrow, Li, t1), voff);
     }
     if (more) pf.store(tiles[(w + 1) & 1]);
     store_lanes<IO, ALIGNED>(window_rsrc(yrow, y_elems, t0), voff, yv, nvalid);
