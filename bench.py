@@ -479,7 +479,7 @@ def bench_codec(args):
         "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.tokens, "d_model": w.d_model, "parts": P, "block": block,
-                   "io": w.io, "parallelism": "none (the collective between ranks is not part of this build)"},
+                   "io": w.io, "parallelism": "none (the collective between ranks is not part of the library)"},
         "quantize": {"us": round(q_ms * 1e3, 2), "algorithmic_bytes": qb, "achieved": round(q_gbps, 1),
                      "frac": round(q_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(w.name, "quantize")},
         "dequant_sum": {"us": round(d_ms * 1e3, 2), "algorithmic_bytes": db, "achieved": round(d_gbps, 1),
@@ -781,7 +781,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the channel-local recurrence would shard by channel with no exchange inside it).",
               file=sys.stderr)
         sys.exit(2)

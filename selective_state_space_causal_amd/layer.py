@@ -12,7 +12,7 @@ hipBLASLt GEMMs):
 
 "Scaling State-Space Models on Multiple GPUs with Tensor Parallelism" (euno.news summary of
 arXiv 2602.21144), Methodology items 1-2.  With more than one rank, x_proj's outputs and out
-are partial sums that the ranks add (all-reduces outside this build); on one GPU the slice's
+are partial sums that the ranks add (all-reduces that this library does not run); on one GPU the slice's
 partials are used as they are.
 
 Decode (mixer_decode_step) runs one token per batch row from the cache the prefill left:
