@@ -5,9 +5,12 @@
 //
 // With a single token the product is a matrix-vector one: each weight is used by at most a few
 // batch rows, so the call is bound by streaming W from HBM once, not by arithmetic, and a GEMM
-// tiling for the matrix cores only adds latency.  Here each wave owns 2 rows of W; its lanes
-// walk each row in 16-byte pieces (8 bf16 or 4 fp32 weights), 64 pieces apart, so that the
-// wave reads 1 KiB of contiguous row per load, four loads per row in flight together.
+// tiling for the matrix cores only adds latency.  Here each wave owns one row of W, eight waves
+// to a workgroup; its lanes walk the row in 16-byte pieces (8 bf16 or 4 fp32 weights), 64
+// pieces apart, so that the wave reads 1 KiB of contiguous row per load, four loads in flight
+// together.  (In the 7B-class layer's decode, in_proj and out_proj with M = 4096, this shape,
+// 512 workgroups, made a token 0.5 us faster than two rows per wave in workgroups of four;
+// two rows per wave or unrolling by 8 were slower, 16 waves to a workgroup the same.)
 // Each piece is multiplied by the same piece of every batch row's input (read through the
 // caches: the four waves of a workgroup share it) with fp32 fused multiply-adds; the 64 lane
 // sums of each (row, batch row) are then added across the wave and rounded once to the output
@@ -20,8 +23,8 @@
 namespace ssm {
 namespace {
 
-constexpr int kRowsPerWave = 2;
-constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 1;
+constexpr int kWaves = 8;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 constexpr int kMaxGroup = 8;  // batch rows per pass over W
 
@@ -61,8 +64,8 @@ __device__ __forceinline__ void store_out(float v, uint16_t* p) {
 }
 __device__ __forceinline__ void store_out(float v, float* p) { *p = v; }
 
-// Batch rows b0 .. b0 + NB - 1; rows of W row0 .. row0 + 1 of this wave (clamped into W; only
-// rows below M are stored).
+// Batch rows b0 .. b0 + NB - 1; rows of W row0 .. row0 + kRowsPerWave - 1 of this wave (clamped
+// into W; only rows below M are stored).
 template <typename IO, typename OUT, int NB>
 __device__ __forceinline__ void gemv_group(const IO* __restrict__ in, const IO* __restrict__ w, OUT* __restrict__ out,
                                            int K, int M, int b0, int row0) {
