@@ -9,7 +9,7 @@
 //                  block's conv front from the cache (rounded to the io dtype, as the unfused layer
 //                  stores u), then the channel block's share of 64 of the R + 2N x_proj outputs,
 //                  four threads per output, written as an fp32 partial sum into the workspace;
-//   dt_decode      one workgroup per (batch row, block of 64 channels), four lanes per channel:
+//   dt_decode      one workgroup per (batch row, block of 32 channels), four lanes per channel:
 //                  the batch row's R + 2N outputs as the sum of the blocks' partials (in block
 //                  order, then rounded to the io dtype), then per channel its dt_proj dot product
 //                  split over the four lanes (rounded to the io dtype), then the decode step of
@@ -26,8 +26,13 @@
 namespace ssm {
 namespace {
 
-constexpr int kCB = 64;         // channels per workgroup, both kernels
-constexpr int kThreads = 256;   // threads per workgroup, both kernels (dt_decode: 64 quads)
+constexpr int kCB = 64;         // xproj_partial: channels per workgroup
+constexpr int kThreads = 256;   // xproj_partial: threads per workgroup
+// dt_decode: 32 quads (one channel each) per workgroup, so that the 7B-class slice's 2048
+// channels run as 64 workgroups (0.3 us per token faster than 256 threads and 32 workgroups;
+// 64 threads and 512 threads are 0.9 and 2.4 us slower).
+constexpr int kDtThreads = 128;
+constexpr int kDtCB = kDtThreads / 4;
 constexpr int kNS = 16;         // d_state
 constexpr int kMaxRows = SSM_FUSED_MAX_ROWS;
 
@@ -46,7 +51,8 @@ struct FusedArgs {
   const void* wdt;  // [D, R]
   float* part;      // [B, nblk, M]
   int64_t B, D;
-  int R, M, nblk;
+  int R, M, nblk;  // nblk: xproj_partial's channel blocks
+  int ndb;         // dt_decode's channel blocks
 };
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -153,13 +159,13 @@ constexpr int kMaxQuarter = (kMaxRows - 2 * kNS + 3) / 4;  // a lane's share of 
 // 16-byte pieces.  The channel's weights, state and inputs are loaded before the reduction of
 // the partial sums, which they do not depend on.
 template <typename IO, bool VEC>
-__global__ __launch_bounds__(kThreads) void dt_decode(FusedArgs a) {
+__global__ __launch_bounds__(kDtThreads) void dt_decode(FusedArgs a) {
   __shared__ float rs[kMaxRows];
-  const int64_t b = blockIdx.x / a.nblk;
-  const int blk = (int)(blockIdx.x - b * a.nblk);
+  const int64_t b = blockIdx.x / a.ndb;
+  const int blk = (int)(blockIdx.x - b * a.ndb);
   const int t = threadIdx.x;
   const int q = t & 3;
-  const int64_t c_raw = (int64_t)blk * kCB + (t >> 2);
+  const int64_t c_raw = (int64_t)blk * kDtCB + (t >> 2);
   const bool live = c_raw < a.D;
   const int64_t c = live ? c_raw : a.D - 1;  // a ragged last block repeats the last channel, writes nothing
   const int quarter = (a.R + 3) / 4;
@@ -188,30 +194,35 @@ __global__ __launch_bounds__(kThreads) void dt_decode(FusedArgs a) {
   const float zt = to_f32(static_cast<const IO*>(a.z ? a.z : a.x)[row]);
 
   // This batch row's x_proj outputs: the blocks' partial sums in block order, rounded to io.
-  // A thread sums outputs t and t + kThreads (M <= 2 kThreads), both rows' partials loaded
+  // A thread sums outputs t, t + kDtThreads, ... (kOut of them), all their partials loaded
   // together, so the reads are one round trip per batch of partials (with clamped indices and
   // the values past the end dropped, so that no load sits under a branch).
   const float* pb = a.part + b * a.nblk * a.M;
-  static_assert(kMaxRows <= 2 * kThreads, "two outputs per thread");
-  const int j0 = t, j1 = t + kThreads;
-  const int jc0 = j0 < a.M ? j0 : a.M - 1, jc1 = j1 < a.M ? j1 : a.M - 1;
-  float s0 = 0.0f, s1 = 0.0f;
+  constexpr int kOut = (kMaxRows + kDtThreads - 1) / kDtThreads;
+  int jc[kOut];
+  float sj[kOut];
+#pragma unroll
+  for (int o = 0; o < kOut; ++o) {
+    const int j = t + o * kDtThreads;
+    jc[o] = j < a.M ? j : a.M - 1;
+    sj[o] = 0.0f;
+  }
   for (int k0 = 0; k0 < a.nblk; k0 += kPartBatch) {
-    float v0[kPartBatch], v1[kPartBatch];
+    float v[kOut][kPartBatch];
 #pragma unroll
     for (int i = 0; i < kPartBatch; ++i) {
       const int64_t k = k0 + i < a.nblk ? k0 + i : a.nblk - 1;
-      v0[i] = pb[k * a.M + jc0];
-      v1[i] = pb[k * a.M + jc1];
+#pragma unroll
+      for (int o = 0; o < kOut; ++o) v[o][i] = pb[k * a.M + jc[o]];
     }
 #pragma unroll
-    for (int i = 0; i < kPartBatch; ++i) {  // blocks in order, as the unfused x_proj sums them
-      s0 += k0 + i < a.nblk ? v0[i] : 0.0f;
-      s1 += k0 + i < a.nblk ? v1[i] : 0.0f;
-    }
+    for (int i = 0; i < kPartBatch; ++i)  // blocks in order, as the unfused x_proj sums them
+#pragma unroll
+      for (int o = 0; o < kOut; ++o) sj[o] += k0 + i < a.nblk ? v[o][i] : 0.0f;
   }
-  if (j0 < a.M) rs[j0] = to_f32(from_f32<IO>(s0));
-  if (j1 < a.M) rs[j1] = to_f32(from_f32<IO>(s1));
+#pragma unroll
+  for (int o = 0; o < kOut; ++o)
+    if (t + o * kDtThreads < a.M) rs[t + o * kDtThreads] = to_f32(from_f32<IO>(sj[o]));
   __syncthreads();
 
   // dt_proj of channel c: lane q sums its quarter of the row, the quad adds the quarters.
@@ -262,12 +273,12 @@ __global__ __launch_bounds__(kThreads) void dt_decode(FusedArgs a) {
 
 template <typename IO>
 hipError_t launch(const FusedArgs& a, bool vec_x, bool vec_dt, hipStream_t s) {
-  const dim3 grid((unsigned)(a.B * a.nblk)), block(kThreads);
-  const dim3 xgrid((unsigned)(a.B * a.nblk * ((a.M + kRowsPerWG - 1) / kRowsPerWG)));
-  if (vec_x) xproj_partial<IO, true><<<xgrid, block, 0, s>>>(a);
-  else xproj_partial<IO, false><<<xgrid, block, 0, s>>>(a);
-  if (vec_dt) dt_decode<IO, true><<<grid, block, 0, s>>>(a);
-  else dt_decode<IO, false><<<grid, block, 0, s>>>(a);
+  const dim3 xgrid((unsigned)(a.B * a.nblk * ((a.M + kRowsPerWG - 1) / kRowsPerWG))), xblock(kThreads);
+  const dim3 dgrid((unsigned)(a.B * a.ndb)), dblock(kDtThreads);
+  if (vec_x) xproj_partial<IO, true><<<xgrid, xblock, 0, s>>>(a);
+  else xproj_partial<IO, false><<<xgrid, xblock, 0, s>>>(a);
+  if (vec_dt) dt_decode<IO, true><<<dgrid, dblock, 0, s>>>(a);
+  else dt_decode<IO, false><<<dgrid, dblock, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -289,7 +300,9 @@ bool fused_sizes(const ssm_dims* d, int64_t rank, int64_t* nblk, int64_t* ws_byt
   *nblk = (d->d_inner + kCB - 1) / kCB;
   const int64_t nrb = (rank + 2 * kNS + kRowsPerWG - 1) / kRowsPerWG;  // x_proj row blocks
   int64_t t;
+  const int64_t ndb = (d->d_inner + kDtCB - 1) / kDtCB;  // dt_decode's channel blocks
   if (__builtin_mul_overflow(d->batch, *nblk, &t) || t * nrb >= ((int64_t)1 << 31) ||
+      d->batch * ndb >= ((int64_t)1 << 31) ||
       __builtin_mul_overflow(t, (rank + 2 * kNS) * 4, ws_bytes) ||
       __builtin_mul_overflow(d->batch, d->d_inner * kNS * 4, &t))
     return false;
@@ -379,6 +392,7 @@ ssm_status decode_fused(const ssm_dims* d, const ssm_params* p, const void* w_x,
   a.R = (int)rank;
   a.M = (int)M;
   a.nblk = (int)nblk;
+  a.ndb = (int)((D + kDtCB - 1) / kDtCB);
   const bool vec_x = D % 8 == 0 && aligned(w_x, 16);
   const bool vec_dt = rank % 32 == 0 && aligned(w_dt, 16);
   (void)hipGetLastError();  // drop a stale error so a launch failure is reported as ours
