@@ -31,9 +31,15 @@
 //   - while a wave multiplies step s, it computes u of step s + 1 into the other u tile, a
 //     quarter after each of the four 16-channel slices of products (the matrix cores run a
 //     product while the vector units compute); one barrier per step.
-// Loads are unconditional (indices clamped into the tensors; u past D is zeroed where it is
-// made, and W past D or M holds copies of in-range weights that meet u = 0 or feed dropped
-// rows), so no lane branches around a load.  The sums are rounded to bf16 (nearest even) once,
+// Loads are unconditional within a wave (indices clamped into the tensors; u past D is zeroed
+// where it is made, and W past D or M holds copies of in-range weights that meet u = 0 or feed
+// dropped rows), so no lane branches around a load; the step's conv weights are loaded and
+// stored by the first wave alone (a wave-uniform branch: seven of eight waves issue no load for
+// them).  The clamps, the cache history and the zeroing past D are compiled only into the general
+// form of the loop, which runs in the first workgroup of each batch row (whose first group
+// starts the row) and, when D is not a multiple of 64, in every workgroup; the others run a form
+// whose x and W offsets are the same in every step (W's step offset is a scalar operand) and
+// whose conv history is the 4 raw inputs before each group.  The sums are rounded to bf16 (nearest even) once,
 // at the end, staged through LDS and written as whole 16-byte pieces of the output rows.
 #include <string.h>
 
@@ -114,7 +120,9 @@ struct WRegs {
 
 
 // Every thread issues the same loads in every step (no load sits under a branch), so that the
-// wait for a set loaded two steps ago leaves the later loads in flight.
+// wait for a set loaded two steps ago leaves the later loads in flight.  HEAD: the workgroup's
+// first group may start a row (t0 = 0); RAG: the step may hold channels past D.
+template <bool HEAD, bool RAG>
 __device__ __forceinline__ void load_x(const XprojArgs& a, int64_t b, int64_t t0, int64_t k0, XRegs& r) {
   const int g = threadIdx.x >> 5;
   const int64_t t = t0 + 8 * g;
@@ -124,15 +132,23 @@ __device__ __forceinline__ void load_x(const XprojArgs& a, int64_t b, int64_t t0
   const bool head = t == 0 && a.conv0 != nullptr;  // history from the cache
   // the step's block of channel rows through a buffer view (uniform base, 32-bit lane offsets;
   // the offsets stay inside it, clamped as above)
-  const int rows = a.D - k0 < KC ? (int)(a.D - k0) : KC;
+  const int rows = !RAG ? KC : a.D - k0 < KC ? (int)(a.D - k0) : KC;
   const auto rx = rsrc(static_cast<const char*>(a.x) + (b * a.D + k0) * a.L * 2, (int64_t)rows * a.L * 2);
 #pragma unroll
   for (int h = 0; h < CPT; ++h) {
     const int c = (threadIdx.x & 31) + 32 * h;
-    const int cc = c < rows ? c : rows - 1;
+    const int cc = !RAG ? c : c < rows ? c : rows - 1;
     // raw values: channels past D give u = 0 in conv_piece, tokens past L only outputs that
     // are not stored
     r.xv[h] = __builtin_amdgcn_raw_buffer_load_b128(rx, (cc * (int)a.L + (int)tl) * 2, 0, 0);
+    if constexpr (!HEAD) {
+      // no group of this workgroup starts a row (t0 >= 128, so tl >= 120): the history is the
+      // raw inputs before it (the last 3 of the 4 read are used)
+      const u32x2 hv = __builtin_amdgcn_raw_buffer_load_b64(rx, (cc * (int)a.L + (int)tl - 4) * 2, 0, 0);
+      r.xh[h][1] = hv[0];
+      r.xh[h][2] = hv[1];
+      continue;
+    }
     // one load from one of two places (an address select, not a branch)
     const uintptr_t px = reinterpret_cast<uintptr_t>(static_cast<const char*>(a.x) + (b * a.D + k0) * a.L * 2) +
                          (uint32_t)((cc * (int)a.L + (tl >= 6 ? (int)tl - 6 : 0)) * 2);
@@ -169,6 +185,7 @@ __device__ __forceinline__ WSlots w_slots(const XprojArgs& a, int m0) {
   return ws;
 }
 
+template <bool RAG>
 __device__ __forceinline__ void dma_w(const XprojArgs& a, int64_t k0, const WSlots& ws, uint16_t* wt) {
   // 32-bit offsets: the caller keeps W below 2 GiB
   const auto rw = rsrc(a.w, (int64_t)a.M * a.D * 2);
@@ -176,18 +193,25 @@ __device__ __forceinline__ void dma_w(const XprojArgs& a, int64_t k0, const WSlo
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
-    const int o = ws.off[i] + k2 < ws.lim[i] ? ws.off[i] + k2 : ws.lim[i];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(wt + (i * THREADS + 64 * wave) * 8),
-                                             16, o, 0, 0, 0);
+    if constexpr (RAG) {
+      const int o = ws.off[i] + k2 < ws.lim[i] ? ws.off[i] + k2 : ws.lim[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(wt + (i * THREADS + 64 * wave) * 8),
+                                               16, o, 0, 0, 0);
+    } else {
+      // D a multiple of KC: every chunk of every step is in range (off + 2 k0 <= lim)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void*)(wt + (i * THREADS + 64 * wave) * 8),
+                                               16, ws.off[i], k2, 0, 0);
+    }
   }
 }
 
 // The conv weights of step kc: thread t reads channel kc + t % KC's taps (float4) and bias
-// (all threads the same loads; clamped past D, and without a bias the taps are read again).
+// (clamped past D, and without a bias the taps are read again).
+template <bool RAG>
 __device__ __forceinline__ void load_cw(const XprojArgs& a, int64_t kc, WRegs& r) {
   const int last = (int)(a.D - 1 - kc);  // channels kc .. kc + last exist
   const int i = threadIdx.x % KC;
-  const int ii = i <= last ? i : last;
+  const int ii = !RAG ? i : i <= last ? i : last;
   const auto rw = rsrc(a.conv_w + kc * 4, (int64_t)(last + 1) * 16);
   r.cv = __builtin_amdgcn_raw_buffer_load_b128(rw, ii * 16, 0, 0);
   const auto rb = a.conv_b ? rsrc(a.conv_b + kc, (int64_t)(last + 1) * 4) : rw;
@@ -195,10 +219,11 @@ __device__ __forceinline__ void load_cw(const XprojArgs& a, int64_t kc, WRegs& r
 }
 
 // Threads 0 .. KC - 1 store their channel's taps and bias ([KC] float4, then [KC] float).
+template <bool RAG>
 __device__ __forceinline__ void store_cw(const XprojArgs& a, int64_t kc, const WRegs& r, float* ct) {
   const int t = threadIdx.x;
   if (t < KC) {
-    const bool ok = t <= (int)(a.D - 1 - kc);
+    const bool ok = !RAG || t <= (int)(a.D - 1 - kc);
     *reinterpret_cast<u32x4*>(&ct[4 * t]) = ok ? r.cv : u32x4{0u, 0u, 0u, 0u};
     ct[4 * KC + t] = ok && a.conv_b ? __uint_as_float(r.cb) : 0.0f;
   }
@@ -223,7 +248,7 @@ __device__ __forceinline__ ConvW read_convw(const float* ct) {
 
 // u of tokens 4 HALF .. 4 HALF + 3 of this thread's channel H, bf16, into the transposed tile
 // (nch: channels of the step below D).
-template <int H, int HALF>
+template <int H, int HALF, bool HEAD, bool RAG>
 __device__ __forceinline__ void conv_piece(const XRegs& r, const ConvW& q, bool head, bool cache, int nch,
                                            uint16_t* ut) {
   const int g = threadIdx.x >> 5;
@@ -232,9 +257,15 @@ __device__ __forceinline__ void conv_piece(const XRegs& r, const ConvW& q, bool 
   if (HALF == 0) {
     // a row's first group (head) takes the cached inputs (zero without a cache); the others
     // tokens t - 3 .. t - 1: the high half of the second pair and the third pair
-    xv[0] = head ? (cache ? __uint_as_float(r.xh[H][0]) : 0.0f) : __uint_as_float(r.xh[H][1] & 0xFFFF0000u);
-    xv[1] = head ? (cache ? __uint_as_float(r.xh[H][1]) : 0.0f) : __uint_as_float(r.xh[H][2] << 16);
-    xv[2] = head ? (cache ? __uint_as_float(r.xh[H][2]) : 0.0f) : __uint_as_float(r.xh[H][2] & 0xFFFF0000u);
+    if constexpr (HEAD) {
+      xv[0] = head ? (cache ? __uint_as_float(r.xh[H][0]) : 0.0f) : __uint_as_float(r.xh[H][1] & 0xFFFF0000u);
+      xv[1] = head ? (cache ? __uint_as_float(r.xh[H][1]) : 0.0f) : __uint_as_float(r.xh[H][2] << 16);
+      xv[2] = head ? (cache ? __uint_as_float(r.xh[H][2]) : 0.0f) : __uint_as_float(r.xh[H][2] & 0xFFFF0000u);
+    } else {
+      xv[0] = __uint_as_float(r.xh[H][1] & 0xFFFF0000u);
+      xv[1] = __uint_as_float(r.xh[H][2] << 16);
+      xv[2] = __uint_as_float(r.xh[H][2] & 0xFFFF0000u);
+    }
     xv[3] = __uint_as_float(r.xv[H][0] << 16);
     xv[4] = __uint_as_float(r.xv[H][0] & 0xFFFF0000u);
     xv[5] = __uint_as_float(r.xv[H][1] << 16);
@@ -254,7 +285,7 @@ __device__ __forceinline__ void conv_piece(const XRegs& r, const ConvW& q, bool 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float v = fmaf(w4.w, xv[3 + j], fmaf(w4.z, xv[2 + j], fmaf(w4.y, xv[1 + j], fmaf(w4.x, xv[j], cb))));
-    uv[j >> 1][j & 1] = c < nch ? silu(v) : 0.0f;  // channels past D: exactly zero
+    uv[j >> 1][j & 1] = !RAG || c < nch ? silu(v) : 0.0f;  // channels past D: exactly zero
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {  // round to bf16, nearest even (v_cvt_pk_bf16_f32)
@@ -269,6 +300,7 @@ __device__ __forceinline__ void conv_piece(const XRegs& r, const ConvW& q, bool 
 // of the next slice are read first, then the slice's five products are issued one at a time with
 // a quarter of the conv front's arithmetic between them (the matrix cores run a product while
 // the vector units compute), then that quarter's u is written.
+template <bool HEAD, bool RAG>
 __device__ __forceinline__ void step_products(f32x16 (&acc)[MB_PER_WAVE], const uint16_t* ut, const uint16_t* wt,
                                               int tb, int mset, const XRegs& X, bool head, bool cache, int nch,
                                               const float* ct, uint16_t* nu) {
@@ -290,10 +322,10 @@ __device__ __forceinline__ void step_products(f32x16 (&acc)[MB_PER_WAVE], const 
     if (ks + 1 < KC / 16) frags(ks + 1, f ^ 1);
 #pragma unroll
     for (int i = 0; i < MB_PER_WAVE; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw[f][i], bu[f], acc[i], 0, 0, 0);
-    if (ks == 0) conv_piece<0, 0>(X, q, head, cache, nch, nu);
-    if (ks == 1) conv_piece<0, 1>(X, q, head, cache, nch, nu);
-    if (ks == 2) conv_piece<1, 0>(X, q, head, cache, nch, nu);
-    if (ks == 3) conv_piece<1, 1>(X, q, head, cache, nch, nu);
+    if (ks == 0) conv_piece<0, 0, HEAD, RAG>(X, q, head, cache, nch, nu);
+    if (ks == 1) conv_piece<0, 1, HEAD, RAG>(X, q, head, cache, nch, nu);
+    if (ks == 2) conv_piece<1, 0, HEAD, RAG>(X, q, head, cache, nch, nu);
+    if (ks == 3) conv_piece<1, 1, HEAD, RAG>(X, q, head, cache, nch, nu);
     // order within the slice: next fragments, then product / arithmetic / product ...
     if (ks + 1 < KC / 16) __builtin_amdgcn_sched_group_barrier(0x100, MB_PER_WAVE + 1, 0);
 #pragma unroll
@@ -310,7 +342,7 @@ __device__ __forceinline__ void step_products(f32x16 (&acc)[MB_PER_WAVE], const 
 // end), the conv weights of step s + 2 (into c[P], free since u of step s was made) and x of
 // step s + 2 into XL.  All of it runs in every step, past the last step on repeated data into
 // tiles that are no longer read: no load or wait then depends on a branch.
-template <int P>
+template <int P, bool HEAD, bool RAG>
 __device__ __forceinline__ void pipe_step(const XprojArgs& a, Tiles& tl, WTile& w0, WTile& w1,
                                           f32x16 (&acc)[MB_PER_WAVE], int64_t b,
                                           int64_t t0, int m0, int tb, int mset, bool head, int s, int nsteps,
@@ -319,15 +351,19 @@ __device__ __forceinline__ void pipe_step(const XprojArgs& a, Tiles& tl, WTile& 
   const int64_t kn = (int64_t)(next ? s + 1 : s) * KC;
   const int64_t ka = (int64_t)(after ? s + 2 : nsteps - 1) * KC;
   // issue order: what this step stores at its end first, x last (its wait is two steps away)
-  dma_w(a, kn, ws, P ? w0.w : w1.w);
-  load_cw(a, ka, W);
-  load_x(a, b, t0, ka, XL);
+  dma_w<RAG>(a, kn, ws, P ? w0.w : w1.w);
+  __builtin_amdgcn_sched_barrier(0);  // the tile loads first: the wait at the barrier is for them alone
+  // only the first wave stores the conv weights: the others issue no load for them
+  const bool cw_wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+  if (cw_wave) load_cw<RAG>(a, ka, W);
+  load_x<HEAD, RAG>(a, b, t0, ka, XL);
   const int nch = a.D - kn < KC ? (int)(a.D - kn) : KC;
-  step_products(acc, tl.u[P], P ? w1.w : w0.w, tb, mset, XN, head, a.conv0 != nullptr, nch, tl.c[P ^ 1], tl.u[P ^ 1]);
-  store_cw(a, ka, W, tl.c[P]);
+  step_products<HEAD, RAG>(acc, tl.u[P], P ? w1.w : w0.w, tb, mset, XN, head, a.conv0 != nullptr, nch, tl.c[P ^ 1], tl.u[P ^ 1]);
+  if (cw_wave) store_cw<RAG>(a, ka, W, tl.c[P]);
   __syncthreads();
 }
 
+template <bool HEAD, bool RAG>
 __device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, WTile& w0, WTile& w1,
                                           f32x16 (&acc)[MB_PER_WAVE], int64_t b,
                                           int64_t t0, int m0, int tb, int mset) {
@@ -337,30 +373,30 @@ __device__ __forceinline__ void main_loop(const XprojArgs& a, Tiles& tl, WTile& 
   XRegs X0, X1;
   WRegs W;
   const WSlots ws = w_slots(a, m0);
-  dma_w(a, 0, ws, w0.w);
-  load_cw(a, 0, W);
-  load_x(a, b, t0, 0, X0);
-  load_x(a, b, t0, nsteps > 1 ? KC : 0, X1);
-  store_cw(a, 0, W, tl.c[0]);
+  dma_w<RAG>(a, 0, ws, w0.w);
+  load_cw<RAG>(a, 0, W);
+  load_x<HEAD, RAG>(a, b, t0, 0, X0);
+  load_x<HEAD, RAG>(a, b, t0, nsteps > 1 ? KC : 0, X1);
+  store_cw<RAG>(a, 0, W, tl.c[0]);
   if (nsteps > 1) {
-    load_cw(a, KC, W);
-    store_cw(a, KC, W, tl.c[1]);
+    load_cw<RAG>(a, KC, W);
+    store_cw<RAG>(a, KC, W, tl.c[1]);
   }
   __syncthreads();
   const int nch0 = a.D < KC ? (int)a.D : KC;
   const ConvW q0 = read_convw(tl.c[0]);
-  conv_piece<0, 0>(X0, q0, head, cache, nch0, tl.u[0]);
-  conv_piece<0, 1>(X0, q0, head, cache, nch0, tl.u[0]);
-  conv_piece<1, 0>(X0, q0, head, cache, nch0, tl.u[0]);
-  conv_piece<1, 1>(X0, q0, head, cache, nch0, tl.u[0]);
+  conv_piece<0, 0, HEAD, RAG>(X0, q0, head, cache, nch0, tl.u[0]);
+  conv_piece<0, 1, HEAD, RAG>(X0, q0, head, cache, nch0, tl.u[0]);
+  conv_piece<1, 0, HEAD, RAG>(X0, q0, head, cache, nch0, tl.u[0]);
+  conv_piece<1, 1, HEAD, RAG>(X0, q0, head, cache, nch0, tl.u[0]);
   __syncthreads();
   // Two steps per trip, so that each register set and tile has a fixed role in each half.
   int s = 0;
   for (; s + 1 < nsteps; s += 2) {
-    pipe_step<0>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, ws, W, X0, X1);
-    pipe_step<1>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s + 1, nsteps, ws, W, X1, X0);
+    pipe_step<0, HEAD, RAG>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, ws, W, X0, X1);
+    pipe_step<1, HEAD, RAG>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s + 1, nsteps, ws, W, X1, X0);
   }
-  if (s < nsteps) pipe_step<0>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, ws, W, X0, X1);
+  if (s < nsteps) pipe_step<0, HEAD, RAG>(a, tl, w0, w1, acc, b, t0, m0, tb, mset, head, s, nsteps, ws, W, X0, X1);
 }
 
 // Copy rows [lo, hi) of the stacked output (tensor `out`, width hi - lo) held in the staging
@@ -406,7 +442,14 @@ __global__ __launch_bounds__(THREADS) void conv_xproj_kernel(XprojArgs a) {
   f32x16 acc[MB_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < MB_PER_WAVE; ++i) acc[i] = f32x16{};
-  main_loop(a, tl, w0, w1, acc, b, t0, m0, tb, mset);
+  // The general form (a row's first tokens, channels past D in the last step) only where it is
+  // needed: the first workgroup of each row, and every workgroup when D is not a multiple of KC.
+  if (t0 == 0 || a.D % KC != 0) {
+    if (t0 == 0) main_loop<true, true>(a, tl, w0, w1, acc, b, t0, m0, tb, mset);
+    else main_loop<false, true>(a, tl, w0, w1, acc, b, t0, m0, tb, mset);
+  } else {
+    main_loop<false, false>(a, tl, w0, w1, acc, b, t0, m0, tb, mset);
+  }
 
   // Stage the sums, rounded to bf16, as [token][row] in the W tiles (the last barrier of the loop
   // has freed them; tokens 0..63 in w0, 64..127 in w1): acc[i] register j is row

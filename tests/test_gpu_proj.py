@@ -193,7 +193,8 @@ def bf16_flip_ulps(u64, scale):
 
 @pytest.mark.parametrize("B,Ls,D,R,N,resume", [(1, 256, 64, 8, 16, False), (2, 200, 96, 256, 16, True),
                                                 (1, 136, 40, 300, 16, False), (3, 64, 2048, 48, 16, True),
-                                                (1, 8, 8, 1, 1, False), (2, 520, 136, 160, 16, False)])
+                                                (1, 8, 8, 1, 1, False), (2, 520, 136, 160, 16, False),
+                                                (2, 392, 128, 40, 16, True), (1, 384, 128, 320, 16, False)])
 def test_conv_xproj_matches_oracle(B, Ls, D, R, N, resume):
     """The conv front fused into x_proj against the oracle's conv front, rounded to bf16, then its
     x_proj.  Bound per output: fp32 accumulation (D 2^-24 sum |W u|), the u elements whose bf16
