@@ -12,7 +12,7 @@
 // 512 workgroups, made a token 0.5 us faster than two rows per wave in workgroups of four;
 // two rows per wave or unrolling by 8 were slower, 16 waves to a workgroup the same.)
 // Each piece is multiplied by the same piece of every batch row's input (read through the
-// caches: the four waves of a workgroup share it) with fp32 fused multiply-adds; the 64 lane
+// caches: the eight waves of a workgroup share it) with fp32 fused multiply-adds; the 64 lane
 // sums of each (row, batch row) are then added across the wave and rounded once to the output
 // dtype (bf16: nearest even).  Batch rows are taken up to 8 at a time (W is streamed once per
 // group of 8).
