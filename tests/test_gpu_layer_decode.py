@@ -86,6 +86,27 @@ def test_layer7b_decode_from_a_cache(pj, fused):
     check_steps("layer7b", wts, wd, prm, pd, hidden_all, 0, h, c, f64(h0), f64(c0), pj, fused)
 
 
+@pytest.mark.parametrize("B,DM,D,R", [(3, 64, 200, 64), (2, 48, 196, 24)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_ragged_layer_decode_matches_oracle(pj, B, DM, D, R, fused):
+    """Channel counts that leave a ragged last block in both fused kernels (200 and 196 channels:
+    blocks of 64 in xproj_partial, of 32 in dt_decode), 196 also not a whole number of 16-byte
+    pieces and rank 24 not a multiple of 32 (the element-wise forms of both kernels), several batch
+    rows: 8 decode steps from a random cache, every output against the oracle."""
+    N = 16
+    note(f"ragged layer decode B={B} d_model={DM} d_inner={D} rank={R} fused={fused}")
+    prm = I.make_params_distinct(D, N, seed=D + R)
+    wts = I.make_proj_weights(DM, D, R, N, "bf16", seed=D)
+    hidden_all = I.make_hidden(B, T_STEPS, DM, "bf16", seed=R)
+    wd = weights_on_device(wts)
+    pd = {k: v.to(DEV) for k, v in prm.items() if v is not None}
+    g = torch.Generator().manual_seed(D * R)
+    h0 = torch.randn(B, D, N, generator=g)
+    c0 = torch.randn(B, D, 3, generator=g).to(torch.bfloat16).float()
+    h, c = h0.to(DEV), c0.to(DEV)
+    check_steps(f"ragged D={D}", wts, wd, prm, pd, hidden_all, 0, h, c, f64(h0), f64(c0), pj, fused)
+
+
 def test_fused_and_unfused_decode_agree(pj):
     """The fused stages round at the same points as the separate calls, so from the same cache
     the two paths agree to within the fp32 summation order (which can move a rounded
