@@ -31,7 +31,12 @@
  * With one token per batch row (seqlen 1, a decode step), batch <= 16 and K a multiple of 8
  * (bf16) or 4 (fp32), both layouts are out[b, m] = sum_k W[m, k] in[b, k]: a matrix-vector
  * product bound by reading W from HBM, which runs as a hand-written streaming kernel (fp32
- * fused multiply-adds, W read once per 8 batch rows) instead of a GEMM.
+ * fused multiply-adds, W read once per 8 batch rows) instead of a GEMM.  The token-major-in,
+ * channel-major-out kinds (SSM_PROJ_IN, SSM_PROJ_DT) with bf16 in and out, K a multiple of 16 up
+ * to 256 (the step-size projection, K = its rank), seqlen a multiple of 8 up to 2^24 and
+ * batch x seqlen below 2^30 are bound by writing the output; they run as a hand-written kernel
+ * (the weights of 64 channels held in each wave's registers, 64-token tiles of the input shared
+ * through LDS, fp32 products on the matrix cores, the output rounded to bf16 once).
  *
  * Algorithm choice: hipBLASLt's heuristic offers up to 8 algorithms per shape; for a shape of at
  * least 1e10 flops the first ssm_proj call outside graph capture times each of them on the

@@ -1,7 +1,9 @@
 // ssm_proj.hip -- ssm_proj_* of include/ssm_proj.h: the channel-sliced projections around the
 // scan ("Scaling State-Space Models on Multiple GPUs with Tensor Parallelism", euno.news
 // summary of arXiv 2602.21144, Methodology items 1-2) as hipBLASLt GEMMs on the matrix cores,
-// except one-token calls (a decode step), which ssm_gemv.hip streams as matrix-vector products.
+// except one-token calls (a decode step), which ssm_gemv.hip streams as matrix-vector products,
+// and channel-major outputs with a small inner dimension (the step-size projection), which
+// ssm_lowk.hip runs.
 //
 // hipBLASLt is column-major.  A row-major [R, C] matrix is a column-major [C, R] one, so:
 //   channel-major out (IN, DT): out_b[M, L] (row-major) is column-major [L, M] = in_b * W^T
@@ -21,6 +23,7 @@
 
 #include "../../include/ssm_proj.h"
 #include "ssm_gemv.h"
+#include "ssm_lowk.h"
 
 namespace {
 
@@ -216,6 +219,13 @@ int ssm_proj(ssm_proj_ctx* ctx, int32_t kind, int64_t batch, int64_t seqlen, int
   if (seqlen == 1 && ssm::gemv_fits(batch, in_features, out_features, io_dtype == SSM_BF16))
     return ssm::gemv(io_dtype == SSM_BF16, out_dtype == SSM_BF16, batch, in_features, out_features, in, w, out,
                      static_cast<hipStream_t>(stream))
+               ? SSM_OK
+               : SSM_ERR_LAUNCH;
+  // A small inner dimension with a channel-major output (the step-size projection): bound by
+  // writing the output, streamed by ssm_lowk.hip.
+  if ((kind == SSM_PROJ_IN || kind == SSM_PROJ_DT) &&
+      ssm::lowk_fits(batch, seqlen, in_features, out_features, io_dtype == SSM_BF16, out_dtype == SSM_BF16))
+    return ssm::lowk(batch, seqlen, in_features, out_features, in, w, out, static_cast<hipStream_t>(stream))
                ? SSM_OK
                : SSM_ERR_LAUNCH;
   Plan* p = nullptr;

@@ -51,7 +51,11 @@ def bound(kind, x, w, ref, out_bf16):
                                       (16, 1, 520, 17), (2, 1, 20, 7),
                                       # ... and the GEMM when it does not apply (K not a whole
                                       # number of 16-byte pieces, more than 16 rows)
-                                      (1, 1, 17, 5), (20, 1, 64, 16)])
+                                      (1, 1, 17, 5), (20, 1, 64, 16),
+                                      # token-major in, channel-major out, K a multiple of 16 up to
+                                      # 256: the small-K kernel (tiles across batch rows, channel
+                                      # groups of 512 with a ragged last one, K 16 and 256)
+                                      (3, 200, 256, 600), (1, 40, 16, 1), (2, 24, 160, 130)])
 def test_projection_matches_oracle(pj, kind, io, od, B, Ls, K, M):
     note(f"proj {NAMES[kind]} io={io} out={od} B={B} L={Ls} K={K} M={M}")
     g = torch.Generator().manual_seed(B * 1000 + Ls * 10 + K + kind)
@@ -159,6 +163,29 @@ def test_in_proj_full_size_sampled(pj):
     mag = np.sum(np.abs(hs * ws), axis=1)
     got = x[0, torch.tensor(cs, device=DEV), torch.tensor(ts, device=DEV)].double().cpu().numpy()
     b = w8.d_model * U * mag
+    b = b + 2.0 ** -8 * (np.abs(ref) + b)
+    assert np.all(np.abs(got - ref) <= b)
+
+
+def test_dt_proj_full_size_sampled(pj):
+    """dt_proj of the 7B-class layer at its real size ([1, 32768, 256] x [2048, 256], bf16, the
+    small-K kernel): sampled outputs against fp64 dot products, and the first and last tiles whole."""
+    w8 = I.LAYERS["layer7b"]
+    D, Ls, R = w8.d_inner, w8.seqlen, w8.dt_rank
+    g = torch.Generator(device=DEV).manual_seed(3)
+    lr = torch.randn(1, Ls, R, generator=g, device=DEV).to(torch.bfloat16)
+    wdt = I.make_proj_weights(w8.d_model, D, R, w8.d_state, w8.io, device=DEV)["dt"]
+    dt = pj(L.PROJ_DT, lr, wdt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    cs = np.concatenate([rng.integers(0, D, 600), np.arange(D), np.arange(D)])
+    ts = np.concatenate([rng.integers(0, Ls, 600), np.zeros(D, dtype=np.int64), np.full(D, Ls - 1)])
+    ls = lr[0, torch.tensor(ts, device=DEV)].double().cpu().numpy()
+    ws = wdt[torch.tensor(cs, device=DEV)].double().cpu().numpy()
+    ref = np.sum(ls * ws, axis=1)
+    mag = np.sum(np.abs(ls * ws), axis=1)
+    got = dt[0, torch.tensor(cs, device=DEV), torch.tensor(ts, device=DEV)].double().cpu().numpy()
+    b = R * U * mag
     b = b + 2.0 ** -8 * (np.abs(ref) + b)
     assert np.all(np.abs(got - ref) <= b)
 
