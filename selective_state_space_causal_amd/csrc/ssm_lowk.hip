@@ -19,8 +19,10 @@
 // instruction touched 32 rows and a row got half a line per tile: 70 us for the 7B-class layer's
 // step-size projection, against 60 us for the library GEMM.)  Tokens are flattened over the batch
 // rows (a tile may span two of them; each 8-token piece lies in one, found by a multiply-shift
-// division).  Loads past the last token or channel are clamped into the tensors; their products
-// feed only outputs that are not stored.
+// division).  The workgroups of one token range (one per group of 512 channels) are given ids that
+// land on one XCD, so that they share its L2 copy of the input tiles (the input was fetched past L2
+// once per channel group before: 69 MB against 25 MB).  Loads past the last token or channel are
+// clamped into the tensors; their products feed only outputs that are not stored.
 #include <stdint.h>
 
 #include "ssm_internal.h"
@@ -52,6 +54,7 @@ struct LowkArgs {
   uint64_t l_magic;    // bt / L = (bt * l_magic) >> l_shift for bt < 2^30
   int l_shift;
   int M, ntiles, per;  // per: tiles per workgroup (a contiguous range)
+  int gx;              // channel groups
 };
 
 template <int KS>
@@ -66,7 +69,12 @@ __global__ __launch_bounds__(kThreads) void lowk_kernel(LowkArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c0 = blockIdx.x * kChPerBlock + wave * kChPerWave;  // the wave's first channel
+  // Workgroup id -> (channel group gx, token range gy): consecutive ids go to the 8 XCDs in turn,
+  // so the channel groups of one token range are given ids of one XCD, and share its L2 copy of
+  // the input tiles.
+  const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
+  const int gxi = slot % a.gx, gyi = (slot / a.gx) * 8 + xcd;
+  const int c0 = gxi * kChPerBlock + wave * kChPerWave;  // the wave's first channel
   const bool active = c0 < a.M;                                   // uniform over the wave
 
   // Weight fragments: block j, product s: W[c0 + 32 j + lane % 32][16 s + 8 (lane / 32) .. + 7].
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void lowk_kernel(LowkArgs a) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(wf[j][s]));
 
-  const int first = blockIdx.y * a.per;
+  const int first = gyi * a.per;
   const int last = min(first + a.per, a.ntiles);
   u32x4 pre[PPT];
   auto load_tile = [&](int it) {
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void lowk_kernel(LowkArgs a) {
 
 template <int KS>
 hipError_t launch(const LowkArgs& a, int gx, int gy, hipStream_t s) {
-  lowk_kernel<KS><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, s>>>(a);
+  lowk_kernel<KS><<<dim3((unsigned)(gx * gy)), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -201,7 +209,8 @@ bool lowk(int64_t batch, int64_t seqlen, int64_t in_features, int64_t out_featur
   // about kTargetBlocks workgroups in all (one per CU), each a contiguous range of tiles
   const int want = (kTargetBlocks + gx - 1) / gx;
   a.per = (a.ntiles + want - 1) / want;
-  const int gy = (a.ntiles + a.per - 1) / a.per;
+  const int gy = ((a.ntiles + a.per - 1) / a.per + 7) / 8 * 8;  // a multiple of 8 (ranges past the end are empty)
+  a.gx = gx;
   (void)hipGetLastError();
   hipError_t e;
   switch (in_features / 16) {
