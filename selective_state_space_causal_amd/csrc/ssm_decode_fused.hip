@@ -198,31 +198,61 @@ __global__ __launch_bounds__(kDtThreads) void dt_decode(FusedArgs a) {
   // together, so the reads are one round trip per batch of partials (with clamped indices and
   // the values past the end dropped, so that no load sits under a branch).
   const float* pb = a.part + b * a.nblk * a.M;
-  constexpr int kOut = (kMaxRows + kDtThreads - 1) / kDtThreads;
-  int jc[kOut];
-  float sj[kOut];
+  if constexpr (VEC) {
+    // R a multiple of 32 and N = 16, so M is a multiple of 4: thread t sums outputs 4t .. 4t + 3,
+    // each block's four partials one 16-byte load.
+    const int j0 = 4 * t;
+    const int jc = j0 < a.M ? j0 : a.M - 4;
+    float4 s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < a.nblk; k0 += kPartBatch) {
+      float4 v[kPartBatch];
 #pragma unroll
-  for (int o = 0; o < kOut; ++o) {
-    const int j = t + o * kDtThreads;
-    jc[o] = j < a.M ? j : a.M - 1;
-    sj[o] = 0.0f;
-  }
-  for (int k0 = 0; k0 < a.nblk; k0 += kPartBatch) {
-    float v[kOut][kPartBatch];
+      for (int i = 0; i < kPartBatch; ++i) {
+        const int64_t k = k0 + i < a.nblk ? k0 + i : a.nblk - 1;
+        v[i] = *reinterpret_cast<const float4*>(pb + k * a.M + jc);
+      }
 #pragma unroll
-    for (int i = 0; i < kPartBatch; ++i) {
-      const int64_t k = k0 + i < a.nblk ? k0 + i : a.nblk - 1;
+      for (int i = 0; i < kPartBatch; ++i) {  // blocks in order, as the unfused x_proj sums them
+        const bool in = k0 + i < a.nblk;
+        s4.x += in ? v[i].x : 0.0f;
+        s4.y += in ? v[i].y : 0.0f;
+        s4.z += in ? v[i].z : 0.0f;
+        s4.w += in ? v[i].w : 0.0f;
+      }
+    }
+    if (j0 < a.M) {
+      rs[j0] = to_f32(from_f32<IO>(s4.x));
+      rs[j0 + 1] = to_f32(from_f32<IO>(s4.y));
+      rs[j0 + 2] = to_f32(from_f32<IO>(s4.z));
+      rs[j0 + 3] = to_f32(from_f32<IO>(s4.w));
+    }
+  } else {
+    constexpr int kOut = (kMaxRows + kDtThreads - 1) / kDtThreads;
+    int jc[kOut];
+    float sj[kOut];
 #pragma unroll
-      for (int o = 0; o < kOut; ++o) v[o][i] = pb[k * a.M + jc[o]];
+    for (int o = 0; o < kOut; ++o) {
+      const int j = t + o * kDtThreads;
+      jc[o] = j < a.M ? j : a.M - 1;
+      sj[o] = 0.0f;
+    }
+    for (int k0 = 0; k0 < a.nblk; k0 += kPartBatch) {
+      float v[kOut][kPartBatch];
+#pragma unroll
+      for (int i = 0; i < kPartBatch; ++i) {
+        const int64_t k = k0 + i < a.nblk ? k0 + i : a.nblk - 1;
+#pragma unroll
+        for (int o = 0; o < kOut; ++o) v[o][i] = pb[k * a.M + jc[o]];
+      }
+#pragma unroll
+      for (int i = 0; i < kPartBatch; ++i)  // blocks in order, as the unfused x_proj sums them
+#pragma unroll
+        for (int o = 0; o < kOut; ++o) sj[o] += k0 + i < a.nblk ? v[o][i] : 0.0f;
     }
 #pragma unroll
-    for (int i = 0; i < kPartBatch; ++i)  // blocks in order, as the unfused x_proj sums them
-#pragma unroll
-      for (int o = 0; o < kOut; ++o) sj[o] += k0 + i < a.nblk ? v[o][i] : 0.0f;
+    for (int o = 0; o < kOut; ++o)
+      if (t + o * kDtThreads < a.M) rs[t + o * kDtThreads] = to_f32(from_f32<IO>(sj[o]));
   }
-#pragma unroll
-  for (int o = 0; o < kOut; ++o)
-    if (t + o * kDtThreads < a.M) rs[t + o * kDtThreads] = to_f32(from_f32<IO>(sj[o]));
   __syncthreads();
 
   // dt_proj of channel c: lane q sums its quarter of the row, the quad adds the quarters.
