@@ -424,7 +424,7 @@ ssm_status decode_fused(const ssm_dims* d, const ssm_params* p, const void* w_x,
   a.nblk = (int)nblk;
   a.ndb = (int)((D + kDtCB - 1) / kDtCB);
   const bool vec_x = D % 8 == 0 && aligned(w_x, 16);
-  const bool vec_dt = rank % 32 == 0 && aligned(w_dt, 16);
+  const bool vec_dt = rank % 32 == 0 && aligned(w_dt, 16) && aligned(workspace, 16);  // 16-byte partial loads
   (void)hipGetLastError();  // drop a stale error so a launch failure is reported as ours
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = d->io_dtype == SSM_BF16 ? launch<bf16_t>(a, vec_x, vec_dt, s) : launch<float>(a, vec_x, vec_dt, s);
